@@ -1,0 +1,149 @@
+"""Exact attention in float64 and the running-softmax loop (oracle; test infrastructure only).
+
+[P2] "Fused attention kernel", Overview: attention is softmax(Q K^T) V; a fused
+kernel reaches the same result block by block with a running row maximum and
+row sum, so the fused loop is exact up to rounding order.  Implementation
+sketch: per key block, s = q k_j^T, m_new = max(m, rowmax s),
+alpha = exp(m - m_new), p = exp(s - m_new), l = alpha l + rowsum p,
+o = alpha o + p v_j; at the end o / l and lse = m + log l.  The card scores
+every key block (its note on the printed loop bound of the paper's Algorithm 2)
+and rescales the output by exp(old max - new max) (its note on Algorithm 1).
+
+Readings taken here (the pages leave them open):
+  * softmax scale 1/sqrt(d) on the scores (the sketch prints none);
+  * LSE is the natural log of sum_j exp(scaled score);
+  * causal (query and key sequences of equal length): key j is visible to
+    query i iff j <= i;
+  * the reference precision is float64 ([P2] Variants / 8-bit forward pass
+    compares against FP64; [P1] "How it gets verified" says 32-bit; float64 is
+    the stricter of the two).
+"""
+
+import math
+
+import numpy as np
+
+from .quantize import dequantize
+
+
+def _rows_attention(q_rows, row_idx, k, v, causal, scale):
+    """Attention for the given query rows of one head; float64 in and out."""
+    s = (q_rows @ k.T) * scale
+    if causal:
+        key_idx = np.arange(k.shape[0])
+        s = np.where(key_idx[None, :] <= row_idx[:, None], s, -np.inf)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    o = (p @ v) / l[:, None]
+    return o, m + np.log(l)
+
+
+def attention_fp64(q, k, v, causal, scale, rows=None, row_chunk=512):
+    """softmax(scale * Q K^T [+ causal mask]) V and its log-sum-exp, in float64.
+
+    q, k, v: arrays [..., N, d] (any float type, upcast exactly).  ``rows``
+    optionally restricts the queries to those row indices (same for every
+    leading index).  Returns (O [..., R, d], LSE [..., R]) with R = N or len(rows).
+    The N x N score matrix is never held whole: queries go in chunks.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape[-2], q.shape[-1]
+    lead = q.shape[:-2]
+    row_idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty(lead + (len(row_idx), d), dtype=np.float64)
+    lse = np.empty(lead + (len(row_idx),), dtype=np.float64)
+    for idx in np.ndindex(*lead):
+        qh, kh, vh = q[idx], k[idx], v[idx]
+        for c0 in range(0, len(row_idx), row_chunk):
+            ri = row_idx[c0:c0 + row_chunk]
+            oc, lc = _rows_attention(qh[ri], ri, kh, vh, causal, scale)
+            o[idx + (slice(c0, c0 + len(ri)),)] = oc
+            lse[idx + (slice(c0, c0 + len(ri)),)] = lc
+    return o, lse
+
+
+def reference_attention(q, k, v, causal, rows=None):
+    """R: exact attention of the float32 inputs in float64 with scale 1/sqrt(d)."""
+    d = np.shape(q)[-1]
+    return attention_fp64(q, k, v, causal, 1.0 / math.sqrt(d), rows=rows)
+
+
+def emulated_fp8_attention(q8, k8, v8, q_descale, k_descale, v_descale,
+                           scale_block, hadamard, causal, rows=None):
+    """E1: exact float64 attention of the dequantised FP8 inputs.
+
+    Q^ = e4m3(q8) * descale_q per block (likewise K^, V^).  With the rotation
+    on, Q^ K^^T = d * (Q K^T) up to quantisation error, because the sign
+    diagonal and the unnormalised Hadamard matrix satisfy (S H)(S H)^T = d I;
+    so the score scale is 1/(sqrt(d) * d).  P is not quantised here: this is
+    attention of the quantised inputs, the quantity the FP8 kernel approximates.
+    """
+    d = np.shape(q8)[-1]
+    qh = dequantize(q8, q_descale, scale_block)
+    kh = dequantize(k8, k_descale, scale_block)
+    vh = dequantize(v8, v_descale, scale_block)
+    scale = 1.0 / math.sqrt(d)
+    if hadamard:
+        scale /= d
+    return attention_fp64(qh, kh, vh, causal, scale, rows=rows)
+
+
+def online_attention_fp64(q, k, v, causal, scale, block_c):
+    """The sketch's running-softmax loop for one head, float64, key blocks of ``block_c``.
+
+    Scores every key block including a short last one; rescales the old state
+    by exp(m_old - m_new).  Used only to pin ``attention_fp64`` (they must agree).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape
+    nk = k.shape[0]
+    o = np.zeros((n, d))
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    qi = np.arange(n)
+    for j0 in range(0, nk, block_c):
+        kj = k[j0:j0 + block_c]
+        vj = v[j0:j0 + block_c]
+        s = (q @ kj.T) * scale
+        if causal:
+            kidx = np.arange(j0, j0 + kj.shape[0])
+            s = np.where(kidx[None, :] <= qi[:, None], s, -np.inf)
+        m_new = np.maximum(m, s.max(axis=1))
+        # a row with no visible key yet keeps m = -inf; use 0 as its exp reference
+        ref = np.where(np.isfinite(m_new), m_new, 0.0)
+        alpha = np.exp(np.where(np.isfinite(m), m - ref, -np.inf))
+        p = np.exp(s - ref[:, None])
+        l = alpha * l + p.sum(axis=1)
+        o = alpha[:, None] * o + p @ vj
+        m = m_new
+    return o / l[:, None], m + np.log(l)
+
+
+def brute_force_attention(q, k, v, causal, scale):
+    """Explicit Python loops over rows, keys and channels (tiny inputs only)."""
+    n, d = len(q), len(q[0])
+    nk = len(k)
+    o = [[0.0] * d for _ in range(n)]
+    lse = [0.0] * n
+    for i in range(n):
+        scores = []
+        for j in range(nk):
+            if causal and j > i:
+                continue
+            dot = 0.0
+            for c in range(d):
+                dot += float(q[i][c]) * float(k[j][c])
+            scores.append((j, dot * scale))
+        mx = max(sc for _, sc in scores)
+        total = sum(math.exp(sc - mx) for _, sc in scores)
+        for j, sc in scores:
+            w = math.exp(sc - mx) / total
+            for c in range(d):
+                o[i][c] += w * float(v[j][c])
+        lse[i] = mx + math.log(total)
+    return np.array(o), np.array(lse)

@@ -1,0 +1,92 @@
+"""Rotate + per-block scale + e4m3 encode of Q, K, V (oracle; test infrastructure only).
+
+[P2] "Fused attention kernel", Variants / 8-bit forward pass (FP8, Hopper):
+  * block quantisation: every block of Q, K and V gets its own scale instead of
+    one scale per tensor;
+  * incoherent processing: Q and K (not V) are multiplied by an orthogonal
+    matrix, a random sign diagonal times a Hadamard matrix, before they are
+    quantised.
+[P3] FLAMIA, 4.3 Ablation Study: quantisation fused into one launch, and score
+scales folded together (the 1/d of the unnormalised Hadamard and the block
+descales fold into the score scale on the attention side).
+
+The pages leave the block shape, the scale formula and the rounding open.
+Readings taken here:
+  * a block is ``scale_block`` consecutive tokens of one (batch, head) times all
+    d channels; the last block of a sequence may be short and its maximum is
+    taken over its valid tokens only;
+  * with y the (rotated) float32 block and a = max |y| over the block:
+      inv = fl32(448 / a),  descale = fl32(a / 448)   (correctly rounded float32
+      division); a block of zeros gets inv = descale = 1;
+  * code = e4m3(fl32(y * inv)) with the encoder of ``oracle.e4m3``;
+  * rotation: y = x * sigma (exact), then the float32 fast Walsh-Hadamard
+    transform of ``oracle.hadamard`` (unnormalised, stage order fixed).
+Dequantised value: e4m3_value(code) * descale.
+
+Everything below is float32 numpy arithmetic, which rounds every operation to
+nearest even, so the result is the bit pattern the specification defines.
+"""
+
+import numpy as np
+
+from . import e4m3
+from .hadamard import fwht_f32
+from .philox import sign_vector
+
+_F448 = np.float32(448.0)
+
+
+def num_blocks(n, scale_block):
+    return -(-n // scale_block)
+
+
+def rotate(x, signs):
+    """x @ diag(signs) @ H_d along the last axis, float32 (signs exact +-1)."""
+    y = np.asarray(x, dtype=np.float32) * np.asarray(signs, dtype=np.float32)
+    return fwht_f32(y)
+
+
+def quantize_tensor(x, scale_block, signs=None):
+    """One tensor [..., N, d] -> (codes uint8 [..., N, d], descale float32 [..., nblk]).
+
+    ``signs`` (float32 +-1 of length d) turns the rotation on; None leaves x unrotated.
+    """
+    y = np.asarray(x, dtype=np.float32)
+    if signs is not None:
+        y = rotate(y, signs)
+    n, d = y.shape[-2], y.shape[-1]
+    nb = num_blocks(n, scale_block)
+    lead = y.shape[:-2]
+    amax = np.empty(lead + (nb,), dtype=np.float32)
+    for blk in range(nb):
+        rows = y[..., blk * scale_block:min(n, (blk + 1) * scale_block), :]
+        amax[..., blk] = np.abs(rows).max(axis=(-2, -1))
+    zero = amax == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        inv = np.where(zero, np.float32(1.0), _F448 / amax).astype(np.float32)
+        descale = np.where(zero, np.float32(1.0), amax / _F448).astype(np.float32)
+    inv_rows = np.repeat(inv, scale_block, axis=-1)[..., :n]
+    v = y * inv_rows[..., None]                 # float32 product, round to nearest even
+    return e4m3.encode(v), descale
+
+
+def quantize_qkv(q, k, v, scale_block, hadamard, seed):
+    """The full pre-processing of one attention call.
+
+    Returns (q8, k8, v8, q_descale, k_descale, v_descale).  Q and K share one
+    sign vector drawn from ``seed``; V is never rotated.
+    """
+    d = np.shape(q)[-1]
+    signs = sign_vector(seed, d) if hadamard else None
+    q8, qd = quantize_tensor(q, scale_block, signs)
+    k8, kd = quantize_tensor(k, scale_block, signs)
+    v8, vd = quantize_tensor(v, scale_block, None)
+    return q8, k8, v8, qd, kd, vd
+
+
+def dequantize(codes, descale, scale_block):
+    """float64 value of each code times its block's descale."""
+    vals = e4m3.decode(codes)
+    n = vals.shape[-2]
+    ds = np.repeat(np.asarray(descale, dtype=np.float64), scale_block, axis=-1)[..., :n]
+    return vals * ds[..., None]

@@ -1,0 +1,92 @@
+"""Seeded synthetic inputs for the FP8 attention forward pass.
+
+Shared by the oracle-based tests and by the GPU path's tests and benchmark.
+This module holds no arithmetic of the method: it only draws Q, K, V (float32,
+layout [B][H][N][D]) from numpy's PCG64 generator.
+
+The pages measure on captured activations of two named open-weights models on
+a fixed 8k-token text plus FlashAttention-3's synthetic outlier test ([P1]
+"FP8 attention that keeps FlashAttention-3 throughput at BF16-level accuracy",
+"How it gets verified"; [P2] "Fused attention kernel", 8-bit forward pass).
+The captured activations, weights and text are not available, so every
+workload here is synthetic and stands in for them:
+  * ``outlier``: iid N(0,1) with 0.1% of entries replaced by N(0, 10^2)
+    ([P2] 8-bit forward pass: 0.1% outlier entries; the outlier distribution is
+    not stated on the pages, N(0, 10^2) is the reading taken here);
+  * ``channel``: LLM-like channel outliers: Q and K are N(0,1) with 4 channels
+    per head (the same for Q and K, every batch and token) set to 30 z + 5;
+    V is Student-t with 4 degrees of freedom;
+  * ``iid``: iid N(0,1).
+
+Draw order (fixed): Q, K, V base values; then per tensor the outlier mask and
+outlier values (``outlier``), or the per-head channel ids (``channel``).
+"""
+
+from dataclasses import dataclass, asdict
+
+import numpy as np
+
+SIGN_SEED = 0x5EED     # seed of the random sign diagonal in every configuration
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    causal: bool
+    scale_block: int
+    hadamard: bool
+    kind: str          # "iid" | "outlier" | "channel"
+    data_seed: int
+    sign_seed: int = SIGN_SEED
+
+    def as_dict(self):
+        return asdict(self)
+
+    def flops(self):
+        """Algorithmic FLOPs: 4 d per visible (query, key) pair."""
+        pairs = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+        return 4 * self.D * self.B * self.H * pairs
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 256, 64, False, 64, True, "iid", 0),
+    "outlier": Workload("outlier", 2, 32, 8192, 128, False, 128, True, "outlier", 1),
+    "outlier_causal": Workload("outlier_causal", 2, 32, 8192, 128, True, 128, True, "outlier", 1),
+    "ablation": Workload("ablation", 4, 16, 8448, 128, False, 128, True, "iid", 3),
+    "ablation_tail": Workload("ablation_tail", 4, 16, 8400, 128, False, 128, True, "iid", 3),
+    "channel": Workload("channel", 2, 32, 8192, 128, True, 128, True, "channel", 4),
+    "channel_norot": Workload("channel_norot", 2, 32, 8192, 128, True, 128, False, "channel", 4),
+}
+
+
+def generate(kind, B, H, N, D, seed):
+    """(q, k, v) float32 arrays of shape [B, H, N, D]."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, D)
+    q = rng.standard_normal(size=shape, dtype=np.float32)
+    k = rng.standard_normal(size=shape, dtype=np.float32)
+    if kind == "channel":
+        v = rng.standard_t(4, size=shape).astype(np.float32)
+    else:
+        v = rng.standard_normal(size=shape, dtype=np.float32)
+    if kind == "outlier":
+        for t in (q, k, v):
+            mask = rng.random(size=shape, dtype=np.float32) < 0.001
+            cnt = int(mask.sum())
+            t[mask] = (10.0 * rng.standard_normal(size=cnt, dtype=np.float32)).astype(np.float32)
+    elif kind == "channel":
+        for h in range(H):
+            ch = rng.choice(D, size=4, replace=False)
+            for t in (q, k):
+                t[:, h, :, ch] = np.float32(30.0) * t[:, h, :, ch] + np.float32(5.0)
+    elif kind != "iid":
+        raise ValueError(f"unknown workload kind {kind!r}")
+    return q, k, v
+
+
+def generate_workload(w: Workload):
+    return generate(w.kind, w.B, w.H, w.N, w.D, w.data_seed)
