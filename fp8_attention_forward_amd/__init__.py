@@ -1,0 +1,164 @@
+"""Python binding of the gfx950 FP8 fused attention forward library (libattn_fp8.so).
+
+A thin ctypes layer with the same names as the C ABI (include/attn_fp8.h).  It
+only marshals arguments: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised.
+
+    q8, k8, v8, qd, kd, vd = quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED)
+    o, lse = attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=128, hadamard=True, causal=False)
+    o16, lse16 = attn_bf16_fwd(qb, kb, vb, causal=False)
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "AttnError", "load_library", "quantize_qkv_fp8", "attn_fp8_fwd", "attn_bf16_fwd",
+    "last_error", "abi_version", "EXPORTED_SYMBOLS", "ATTN_OK", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EHIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_fp8.so")
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "attn_fp8_fwd", "attn_bf16_fwd", "attn_fp8_last_error",
+                    "attn_fp8_abi_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def load_library(path=None):
+    """Load libattn_fp8.so (built in place by fp8_attention_forward_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} not found: build it with `python -m fp8_attention_forward_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
+    lib.quantize_qkv_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, u64, vp, vp, vp, vp, vp, vp, vp]
+    lib.quantize_qkv_fp8.restype = i32
+    lib.attn_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.attn_fp8_fwd.restype = i32
+    lib.attn_bf16_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.attn_bf16_fwd.restype = i32
+    lib.attn_fp8_last_error.argtypes = []
+    lib.attn_fp8_last_error.restype = ctypes.c_char_p
+    lib.attn_fp8_abi_version.argtypes = []
+    lib.attn_fp8_abi_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error():
+    return load_library().attn_fp8_last_error().decode()
+
+
+def abi_version():
+    return load_library().attn_fp8_abi_version()
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, last_error())
+
+
+def _ptr(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape4(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, D]")
+    return tuple(int(x) for x in t.shape)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED, out=None):
+    """Rotate (Q, K) + per-block scale + e4m3 encode; returns (q8, k8, v8, q_descale, k_descale, v_descale)."""
+    lib = load_library()
+    B, H, N, D = _shape4(q, "q")
+    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+        raise ValueError("q, k, v must have the same shape")
+    nb = -(-N // scale_block)
+    if out is None:
+        dev = q.device
+        out = tuple(torch.empty((B, H, N, D), dtype=torch.uint8, device=dev) for _ in range(3)) + \
+            tuple(torch.empty((B, H, nb), dtype=torch.float32, device=dev) for _ in range(3))
+    q8, k8, v8, qd, kd, vd = out
+    for t, nm in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if _shape4(t, nm) != (B, H, N, D):
+            raise ValueError(f"{nm} has the wrong shape")
+    for t, nm in ((qd, "q_descale"), (kd, "k_descale"), (vd, "v_descale")):
+        if tuple(t.shape) != (B, H, nb):
+            raise ValueError(f"{nm} must be [B, H, ceil(N/scale_block)]")
+    _check(lib.quantize_qkv_fp8(
+        _ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+        B, H, N, D, int(scale_block), int(bool(hadamard)), int(seed) & 0xFFFFFFFFFFFFFFFF,
+        _ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
+        _ptr(qd, torch.float32, "q_descale"), _ptr(kd, torch.float32, "k_descale"),
+        _ptr(vd, torch.float32, "v_descale"), _stream(q)))
+    return out
+
+
+def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, hadamard=True,
+                 causal=False, out=None):
+    """FP8 attention forward; returns (o [B,H,N,D] bfloat16, lse [B,H,N] float32)."""
+    lib = load_library()
+    B, H, N, D = _shape4(q8, "q8")
+    if _shape4(k8, "k8") != (B, H, N, D) or _shape4(v8, "v8") != (B, H, N, D):
+        raise ValueError("q8, k8, v8 must have the same shape")
+    nb = -(-N // scale_block)
+    for t, nm in ((q_descale, "q_descale"), (k_descale, "k_descale"), (v_descale, "v_descale")):
+        if tuple(t.shape) != (B, H, nb):
+            raise ValueError(f"{nm} must be [B, H, ceil(N/scale_block)]")
+    if out is None:
+        out = (torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q8.device),
+               torch.empty((B, H, N), dtype=torch.float32, device=q8.device))
+    o, lse = out
+    if _shape4(o, "o") != (B, H, N, D) or tuple(lse.shape) != (B, H, N):
+        raise ValueError("o / lse have the wrong shape")
+    _check(lib.attn_fp8_fwd(
+        _ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
+        _ptr(q_descale, torch.float32, "q_descale"), _ptr(k_descale, torch.float32, "k_descale"),
+        _ptr(v_descale, torch.float32, "v_descale"), B, H, N, D, int(scale_block), int(bool(hadamard)),
+        int(bool(causal)), _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _stream(q8)))
+    return out
+
+
+def attn_bf16_fwd(q, k, v, causal=False, out=None):
+    """BF16 attention forward (the 16-bit yardstick); returns (o bfloat16, lse float32)."""
+    lib = load_library()
+    B, H, N, D = _shape4(q, "q")
+    if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
+        raise ValueError("q, k, v must have the same shape")
+    if out is None:
+        out = (torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q.device),
+               torch.empty((B, H, N), dtype=torch.float32, device=q.device))
+    o, lse = out
+    _check(lib.attn_bf16_fwd(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
+        B, H, N, D, int(bool(causal)), _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"),
+        _stream(q)))
+    return out

@@ -1,0 +1,60 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfp8 {
+
+struct QuantParams {
+  const float* q;
+  const float* k;
+  const float* v;
+  uint8_t* q8;
+  uint8_t* k8;
+  uint8_t* v8;
+  float* qd;
+  float* kd;
+  float* vd;
+  int N;
+  int nblk;        // scale blocks per (batch, head) = ceil(N / scale_block)
+  int hadamard;
+  uint32_t key0;   // seed, low word
+  uint32_t key1;   // seed, high word
+};
+
+struct AttnFp8Params {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* qd;
+  const float* kd;
+  const float* vd;
+  uint16_t* o;
+  float* lse;
+  int N;
+  int nblk;          // scale blocks per head (key tile == scale block)
+  int n_qtiles;      // query tiles per head
+  float score_scale; // log2(e) / sqrt(D), divided by D when Q and K were rotated
+};
+
+struct AttnBf16Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int N;
+  int n_qtiles;
+  float score_scale; // log2(e) / sqrt(D)
+};
+
+constexpr int kWaves = 4;              // waves per workgroup in the attention kernels
+constexpr int kQueriesPerWave = 32;
+constexpr int kQueryTile = kWaves * kQueriesPerWave;
+
+hipError_t launch_quantize(const QuantParams& p, int D, int SB, int BH, hipStream_t stream);
+hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int BH, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnBf16Params& p, int D, int causal, int BH, hipStream_t stream);
+
+}  // namespace attnfp8

@@ -1,0 +1,164 @@
+// C ABI entry points: argument validation, device check, launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/attn_fp8.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+// Returns ATTN_OK when the current device is a gfx950.
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_EUNSUPPORTED, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_EUNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(ATTN_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_dev_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (g_dev_state[dev] == 2) return fail(ATTN_EUNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (g_dev_state[dev] != 1) return fail(ATTN_EUNSUPPORTED, "device %d is not gfx950", dev);
+  return ATTN_OK;
+}
+
+int check_sizes(int B, int H, int N, int D) {
+  if (B < 1 || H < 1 || N < 1) return fail(ATTN_EINVAL, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+  if (D != 64 && D != 128) return fail(ATTN_EINVAL, "D must be 64 or 128 (got %d)", D);
+  const long long tiles = (long long)B * H * ((N + attnfp8::kQueryTile - 1) / attnfp8::kQueryTile);
+  if (tiles >= (1LL << 31) || (long long)B * H >= (1LL << 31))
+    return fail(ATTN_EINVAL, "B * H * ceil(N / %d) must be < 2^31", attnfp8::kQueryTile);
+  return ATTN_OK;
+}
+
+int check_sb(int sb) {
+  if (sb != 64 && sb != 128) return fail(ATTN_EINVAL, "scale_block must be 64 or 128 (got %d)", sb);
+  return ATTN_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (p == nullptr) return fail(ATTN_EINVAL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(ATTN_EINVAL, "%s is not %zu-byte aligned", name, align);
+  return ATTN_OK;
+}
+
+#define CHECK(expr)              \
+  do {                           \
+    int _st = (expr);            \
+    if (_st != ATTN_OK) return _st; \
+  } while (0)
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int quantize_qkv_fp8(const float* q, const float* k, const float* v, int B, int H, int N, int D, int scale_block,
+                     int hadamard, uint64_t seed, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* q_descale,
+                     float* k_descale, float* v_descale, void* stream) {
+  CHECK(check_sizes(B, H, N, D));
+  CHECK(check_sb(scale_block));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(q8, 16, "q8"));
+  CHECK(check_ptr(k8, 16, "k8"));
+  CHECK(check_ptr(v8, 16, "v8"));
+  CHECK(check_ptr(q_descale, 4, "q_descale"));
+  CHECK(check_ptr(k_descale, 4, "k_descale"));
+  CHECK(check_ptr(v_descale, 4, "v_descale"));
+  if ((long long)B * H * ((N + scale_block - 1) / scale_block) >= (1LL << 31))
+    return fail(ATTN_EINVAL, "B * H * ceil(N / scale_block) must be < 2^31");
+  CHECK(check_device());
+  attnfp8::QuantParams p;
+  p.q = q; p.k = k; p.v = v;
+  p.q8 = q8; p.k8 = k8; p.v8 = v8;
+  p.qd = q_descale; p.kd = k_descale; p.vd = v_descale;
+  p.N = N;
+  p.nblk = (N + scale_block - 1) / scale_block;
+  p.hadamard = hadamard ? 1 : 0;
+  p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  p.key1 = (uint32_t)(seed >> 32);
+  return launched(attnfp8::launch_quantize(p, D, scale_block, B * H, (hipStream_t)stream), "quantize_qkv_fp8");
+}
+
+int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_descale,
+                 const float* k_descale, const float* v_descale, int B, int H, int N, int D, int scale_block,
+                 int hadamard, int causal, uint16_t* o_bf16, float* lse, void* stream) {
+  CHECK(check_sizes(B, H, N, D));
+  CHECK(check_sb(scale_block));
+  CHECK(check_ptr(q8, 16, "q8"));
+  CHECK(check_ptr(k8, 16, "k8"));
+  CHECK(check_ptr(v8, 16, "v8"));
+  CHECK(check_ptr(q_descale, 4, "q_descale"));
+  CHECK(check_ptr(k_descale, 4, "k_descale"));
+  CHECK(check_ptr(v_descale, 4, "v_descale"));
+  CHECK(check_ptr(o_bf16, 16, "o_bf16"));
+  CHECK(check_ptr(lse, 4, "lse"));
+  CHECK(check_device());
+  attnfp8::AttnFp8Params p;
+  p.q8 = q8; p.k8 = k8; p.v8 = v8;
+  p.qd = q_descale; p.kd = k_descale; p.vd = v_descale;
+  p.o = o_bf16; p.lse = lse;
+  p.N = N;
+  p.nblk = (N + scale_block - 1) / scale_block;
+  p.n_qtiles = (N + attnfp8::kQueryTile - 1) / attnfp8::kQueryTile;
+  double sc = 1.4426950408889634 / std::sqrt((double)D);
+  if (hadamard) sc /= D;
+  p.score_scale = (float)sc;
+  return launched(attnfp8::launch_attn_fp8(p, D, scale_block, causal ? 1 : 0, B * H, (hipStream_t)stream),
+                  "attn_fp8_fwd");
+}
+
+int attn_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N, int D, int causal,
+                  uint16_t* o_bf16, float* lse, void* stream) {
+  CHECK(check_sizes(B, H, N, D));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(o_bf16, 16, "o_bf16"));
+  CHECK(check_ptr(lse, 4, "lse"));
+  CHECK(check_device());
+  attnfp8::AttnBf16Params p;
+  p.q = q; p.k = k; p.v = v;
+  p.o = o_bf16; p.lse = lse;
+  p.N = N;
+  p.n_qtiles = (N + attnfp8::kQueryTile - 1) / attnfp8::kQueryTile;
+  p.score_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+  return launched(attnfp8::launch_attn_bf16(p, D, causal ? 1 : 0, B * H, (hipStream_t)stream), "attn_bf16_fwd");
+}
+
+const char* attn_fp8_last_error(void) { return g_err; }
+
+int attn_fp8_abi_version(void) { return ATTN_FP8_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Device helpers shared by the gfx950 kernels of this library.
+//
+// Lane layouts used below (CDNA4 MFMA, wave64):
+//   * v_mfma_f32_32x32x64_f8f6f4 (fp8 e4m3 operands): lane l holds, for the A
+//     operand, row (l % 32) and the 32 k-values 32*(l/32) .. +31 (one byte
+//     each); the B operand likewise with column (l % 32).  The accumulator
+//     register r of lane l is element (row 8*(r/4) + 4*(l/32) + r%4, col l%32).
+//   * v_mfma_f32_32x32x16_bf16: the same with 8 bf16 k-values per lane,
+//     k = 8*(l/32) .. +7.
+//   * ds_read_b64_tr_b8: within each group of 16 lanes, lane i names an 8-byte
+//     row R_i; lane j receives byte (j % 8) of rows j/8, j/8+2, ..., j/8+14.
+//   * ds_read_b64_tr_b16: lane j receives element (j % 4) of rows j/4, j/4+4,
+//     j/4+8, j/4+12 (four 2-byte elements per row).
+// Only the relation between A and B matters for a contraction, so every
+// permutation of k used here is applied identically to both operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfp8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// fp8 e4m3 x fp8 e4m3 -> fp32, 32x32x64 (scale operands 0 select the unscaled form)
+__device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_bf16(const v4i& a, const v4i& b, const v16f& c) {
+  v8bf av = __builtin_bit_cast(v8bf, a);
+  v8bf bv = __builtin_bit_cast(v8bf, b);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v2i lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(v2i, p));
+}
+
+__device__ __forceinline__ v2i lds_read_tr16(const uint8_t* p) {
+  v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4s, p));
+  return __builtin_bit_cast(v2i, r);
+}
+
+__device__ __forceinline__ v4i lds_read_b128(const uint8_t* p) {
+  return *LDS_PTR(const v4i, p);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void global_to_lds16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, LDS_PTR(void, lds_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// value of lane (l ^ 32)
+__device__ __forceinline__ float swap_halves(float x) {
+  int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
+}
+
+// value of lane (l ^ m) for m < 32 (ds_swizzle bit mode: and 0x1f, xor m)
+template <int M>
+__device__ __forceinline__ float xor_lanes(float x) {
+  static_assert(M > 0 && M < 32, "swizzle xor covers lanes within 32");
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (M << 10) | 0x1F));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, xor_lanes<1>(x));
+  x = fmaxf(x, xor_lanes<2>(x));
+  x = fmaxf(x, xor_lanes<4>(x));
+  x = fmaxf(x, xor_lanes<8>(x));
+  x = fmaxf(x, xor_lanes<16>(x));
+  x = fmaxf(x, swap_halves(x));
+  return x;
+}
+
+// two fp32 -> two e4m3 codes (round to nearest even; inputs must lie in [-448, 448])
+// packed into the low 16 bits (word_sel = false) or high 16 bits of `old`
+template <bool HI>
+__device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Workgroup order: the dispatcher hands consecutive workgroup ids to the 8
+// XCDs in turn.  Remap so that each XCD receives one contiguous range of
+// logical tiles (so the query tiles of a head share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  if (total % 8 != 0) return pid;
+  return (pid % 8) * (total / 8) + pid / 8;
+}
+
+}  // namespace attnfp8

@@ -1,0 +1,160 @@
+// Fused rotate + per-block scale + e4m3 encode of Q, K and V (gfx950).
+//
+// Method ("Fused attention kernel", Variants / 8-bit forward pass (FP8)):
+// every block of Q, K and V gets its own scale, and Q and K are first
+// multiplied by a random sign diagonal times a Hadamard matrix (incoherent
+// processing), which cancels in Q K^T.  FLAMIA (4.3 Ablation Study) fuses the
+// quantisation pre-processing into a single launch; here one launch covers
+// all three tensors.
+//
+// Per workgroup: one (tensor, batch*head, block of SB tokens).  The block
+// (SB x D float32) is read once with coalesced 16-byte loads and kept in
+// registers; each lane holds 4 consecutive channels of a row, D/4 lanes per
+// row.  The unnormalised Sylvester Hadamard transform runs as butterfly
+// stages h = 1, 2 inside the lane and h = 4 .. D/2 across lanes (ds_swizzle
+// xor), always in ascending h so the float32 result is reproducible.  Then
+// amax over the block (wave + LDS reduction), inv = 448/a and descale = a/448
+// (correctly rounded), and code = e4m3(clamp(y * inv, +-448)) with the
+// hardware round-to-nearest-even convert; one 4-byte store per lane per row.
+//
+// Memory: reads 4 B and writes 1 B per element (HBM bound).
+#include "common.h"
+#include "attn_internal.h"
+
+namespace attnfp8 {
+
+// Philox4x32-10 (Salmon et al., SC 2011): one block, counter (0,0,0,0), key = seed.
+__device__ __forceinline__ void philox_block(uint32_t k0, uint32_t k1, uint32_t out[4]) {
+  uint32_t x0 = 0, x1 = 0, x2 = 0, x3 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    uint32_t lo0 = 0xD2511F53u * x0, hi0 = __umulhi(0xD2511F53u, x0);
+    uint32_t lo1 = 0xCD9E8D57u * x2, hi1 = __umulhi(0xCD9E8D57u, x2);
+    uint32_t y0 = hi1 ^ x1 ^ k0, y1 = lo1, y2 = hi0 ^ x3 ^ k1, y3 = lo0;
+    x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+template <int M>
+__device__ __forceinline__ void butterfly_xlane(float (&x)[4], int lane) {
+  // stage pairing lanes (lane, lane ^ M): lower lane keeps a + b, upper keeps a - b
+  const bool upper = (lane & M) != 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float p = xor_lanes<M>(x[e]);
+    x[e] = upper ? (p - x[e]) : (x[e] + p);
+  }
+}
+
+template <int D, int SB>
+__global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
+#pragma clang fp contract(off)
+  constexpr int LPR = D / 4;              // lanes per row
+  constexpr int RPI = 256 / LPR;          // rows per iteration (whole workgroup)
+  constexpr int ITERS = SB / RPI;
+  static_assert(SB % RPI == 0, "block must be a whole number of iterations");
+
+  const int blk = blockIdx.x % p.nblk;
+  const int bh = blockIdx.x / p.nblk;
+  const int tensor = blockIdx.y;          // 0 = Q, 1 = K, 2 = V
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rlane = tid % LPR;            // lane within its row group
+  const int c0 = 4 * rlane;               // first channel held by this lane
+  const float* src = tensor == 0 ? p.q : (tensor == 1 ? p.k : p.v);
+  uint8_t* dst = tensor == 0 ? p.q8 : (tensor == 1 ? p.k8 : p.v8);
+  float* dsc = tensor == 0 ? p.qd : (tensor == 1 ? p.kd : p.vd);
+  const bool rotate = p.hadamard && tensor < 2;
+
+  const size_t head_off = (size_t)bh * p.N * D;
+  const int row0 = blk * SB;
+
+  float x[ITERS][4];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int row = row0 + it * RPI + tid / LPR;
+    if (row < p.N) {
+      v4f t = *(const v4f*)(src + head_off + (size_t)row * D + c0);
+      x[it][0] = t[0]; x[it][1] = t[1]; x[it][2] = t[2]; x[it][3] = t[3];
+    } else {
+      x[it][0] = x[it][1] = x[it][2] = x[it][3] = 0.0f;
+    }
+  }
+
+  if (rotate) {
+    uint32_t w[4];
+    philox_block(p.key0, p.key1, w);
+    float sg[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = c0 + e;
+      sg[e] = ((w[c >> 5] >> (c & 31)) & 1u) ? -1.0f : 1.0f;
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      float (&y)[4] = x[it];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = y[e] * sg[e];
+      // h = 1
+      float a0 = y[0] + y[1], a1 = y[0] - y[1], a2 = y[2] + y[3], a3 = y[2] - y[3];
+      // h = 2
+      y[0] = a0 + a2; y[1] = a1 + a3; y[2] = a0 - a2; y[3] = a1 - a3;
+      // h = 4 .. D/2 across lanes
+      butterfly_xlane<1>(y, rlane);
+      butterfly_xlane<2>(y, rlane);
+      butterfly_xlane<4>(y, rlane);
+      butterfly_xlane<8>(y, rlane);
+      if constexpr (LPR == 32) butterfly_xlane<16>(y, rlane);
+    }
+  }
+
+  // block amax (rows beyond N hold zeros and do not raise it)
+  float m = 0.0f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(x[it][e]));
+  m = wave_max(m);
+  __shared__ float red[4];
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = a == 0.0f ? 1.0f : 448.0f / a;
+  const float descale = a == 0.0f ? 1.0f : a / 448.0f;
+  if (tid == 0) dsc[(size_t)bh * p.nblk + blk] = descale;
+
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int row = row0 + it * RPI + tid / LPR;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(x[it][e] * inv, -448.0f), 448.0f);
+    int packed = cvt_pk_fp8<false>(v[0], v[1], 0);
+    packed = cvt_pk_fp8<true>(v[2], v[3], packed);
+    if (row < p.N) *(int*)(dst + head_off + (size_t)row * D + c0) = packed;
+  }
+}
+
+#define QUANT_INST(D, SB) template __global__ void quantize_qkv_kernel<D, SB>(QuantParams);
+QUANT_INST(64, 64)
+QUANT_INST(64, 128)
+QUANT_INST(128, 64)
+QUANT_INST(128, 128)
+
+hipError_t launch_quantize(const QuantParams& p, int D, int SB, int BH, hipStream_t stream) {
+  dim3 grid(p.nblk * BH, 3);
+  dim3 block(256);
+  if (D == 64 && SB == 64) quantize_qkv_kernel<64, 64><<<grid, block, 0, stream>>>(p);
+  else if (D == 64 && SB == 128) quantize_qkv_kernel<64, 128><<<grid, block, 0, stream>>>(p);
+  else if (D == 128 && SB == 64) quantize_qkv_kernel<128, 64><<<grid, block, 0, stream>>>(p);
+  else quantize_qkv_kernel<128, 128><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace attnfp8

@@ -1,0 +1,113 @@
+/* attn_fp8.h -- C ABI of the MI355X (gfx950) FP8 fused attention forward library.
+ *
+ * The method is the fused running-softmax attention loop described on the page
+ * "Fused attention kernel" (wikillm.com), sections "Overview" and
+ * "Implementation sketch", fed by the 8-bit pre-processing of its section
+ * "Variants / 8-bit forward pass (FP8, Hopper)": incoherent processing (Q and
+ * K multiplied by a random sign diagonal times a Hadamard matrix, which cancels
+ * in Q K^T) and block quantisation to e4m3 with one scale per block of Q, K and
+ * V.  The problem page "FP8 attention that keeps FlashAttention-3 throughput at
+ * BF16-level accuracy", section "How it gets verified", fixes the types: Q, K, V
+ * in E4M3, FP32 softmax statistics, BF16 output; and measures the FP8 error
+ * against the BF16 forward pass, exported here as attn_bf16_fwd.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the caller;
+ *     the library allocates no device memory and keeps no per-call state.
+ *   - Layout is contiguous row-major [B][H][N][D] for Q, K, V, their codes and
+ *     O; [B][H][N] for LSE; [B][H][ceil(N / scale_block)] for block descales.
+ *   - Tensor pointers must be 16-byte aligned; descale and LSE pointers 4-byte.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without synchronising the host; no host copy
+ *     of scales or sizes is made on the device path, so calls can be captured
+ *     in a HIP graph.
+ *   - Supported: D in {64, 128}; scale_block in {64, 128}; B, H, N >= 1;
+ *     B * H * ceil(N / 128) < 2^31.  Only gfx950 devices are supported.
+ *   - Return value: ATTN_OK, or an attn_status error.  On ATTN_EINVAL and
+ *     ATTN_EUNSUPPORTED nothing is launched and no output is written.
+ *     attn_fp8_last_error() then describes the error (per calling thread).
+ *   - Inputs must be finite.  Calls that overlap on one stream are ordered by
+ *     the stream; outputs must not alias inputs.
+ */
+#ifndef ATTN_FP8_H
+#define ATTN_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,       /* bad argument (null/misaligned pointer, unsupported size) */
+  ATTN_EUNSUPPORTED = 2, /* no gfx950 device is current */
+  ATTN_EHIP = 3          /* a HIP runtime call or kernel launch failed */
+} attn_status;
+
+/* quantize_qkv_fp8 -- rotate + per-block scale + e4m3 encode of Q, K and V in
+ * one launch ("Fused attention kernel", 8-bit forward pass: block quantisation
+ * and incoherent processing; fused into one launch as in FLAMIA, 4.3 Ablation
+ * Study).
+ *   q, k, v        in : float32 [B][H][N][D].
+ *   scale_block       : tokens per scale block (64 or 128); a block is
+ *                       scale_block consecutive tokens of one (batch, head)
+ *                       times all D channels; the last block may be short.
+ *   hadamard          : nonzero -> Q and K rows become x * diag(sigma) * H_D
+ *                       (unnormalised Sylvester Hadamard, butterfly stages in
+ *                       ascending order, float32); V is never rotated.
+ *   seed              : 64-bit seed of sigma: one Philox4x32-10 block with
+ *                       counter 0 and key (seed low word, seed high word);
+ *                       sigma_c = -1 when bit c of the 128-bit output is set.
+ *   q8, k8, v8    out : e4m3 codes [B][H][N][D], code = e4m3_rne(clamp(y * inv, +-448))
+ *   q/k/v_descale out : float32 [B][H][ceil(N/scale_block)], descale = amax/448
+ *                       (inv = 448/amax; 1 for an all-zero block).
+ */
+int quantize_qkv_fp8(const float* q, const float* k, const float* v,
+                     int B, int H, int N, int D, int scale_block, int hadamard, uint64_t seed,
+                     uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                     float* q_descale, float* k_descale, float* v_descale, void* stream);
+
+/* attn_fp8_fwd -- FP8 fused attention forward ("Fused attention kernel",
+ * Implementation sketch: running max and sum, exp(old max - new max) rescale,
+ * every key block scored; logsumexp output).
+ *   q8, k8, v8, *_descale in : output of quantize_qkv_fp8 with the same
+ *                       scale_block and hadamard flag (hadamard nonzero folds
+ *                       the 1/D of the unnormalised rotation into the score
+ *                       scale).
+ *   causal            : nonzero -> query i sees keys j <= i.
+ *   o_bf16        out : bf16 bit patterns [B][H][N][D],
+ *                       O = softmax(Q K^T / sqrt(D)) V of the dequantised inputs.
+ *   lse           out : float32 [B][H][N], natural log of sum_j exp(q_i.k_j / sqrt(D)).
+ * Arithmetic: e4m3 x e4m3 products with FP32 accumulation, FP32 statistics,
+ * P re-quantised to e4m3 on chip.
+ */
+int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                 const float* q_descale, const float* k_descale, const float* v_descale,
+                 int B, int H, int N, int D, int scale_block, int hadamard, int causal,
+                 uint16_t* o_bf16, float* lse, void* stream);
+
+/* attn_bf16_fwd -- the same loop on BF16 inputs (BF16 products, FP32
+ * accumulation and statistics, P in BF16), no rotation or quantisation: the
+ * 16-bit yardstick of the problem statement ("What is asked").
+ *   q, k, v      in : bf16 bit patterns [B][H][N][D].
+ *   o_bf16, lse out : as for attn_fp8_fwd.
+ */
+int attn_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  int B, int H, int N, int D, int causal,
+                  uint16_t* o_bf16, float* lse, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none).
+ * The string is owned by the library and valid until the next call on that thread. */
+const char* attn_fp8_last_error(void);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int attn_fp8_abi_version(void);
+
+#define ATTN_FP8_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FP8_H */

@@ -29,7 +29,8 @@ Modules
   hadamard   Sylvester Hadamard matrix and its fast transform [same]
   quantize   rotate + per-block scale + e4m3 encode of Q, K, V [P2 8-bit forward pass]
   attention  exact FP64 attention, the running-softmax loop of the sketch,
-             brute force, and attention of the dequantised FP8 inputs
+             brute force, attention of the dequantised FP8 inputs (E1), and
+             the block loop with P re-quantised to e4m3 (E2)
              [P2 Overview, Implementation sketch]
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` to something
@@ -44,5 +45,6 @@ from .attention import (  # noqa: F401
     online_attention_fp64,
     brute_force_attention,
     emulated_fp8_attention,
+    emulated_fp8_attention_tiled,
 )
 from .quantize import quantize_qkv, quantize_tensor, dequantize  # noqa: F401

@@ -23,6 +23,7 @@ import math
 
 import numpy as np
 
+from . import e4m3
 from .quantize import dequantize
 
 
@@ -147,3 +148,94 @@ def brute_force_attention(q, k, v, causal, scale):
                 o[i][c] += w * float(v[j][c])
         lse[i] = mx + math.log(total)
     return np.array(o), np.array(lse)
+
+
+def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
+                                 causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True):
+    """E2: the running-softmax loop over key blocks with P re-quantised to e4m3.
+
+    The pages fix the loop (Implementation sketch) and that the matrix products
+    run on 8-bit inputs; they are silent on the precision and scale of P.
+    Reading taken here (the FP8 kernel follows it):
+      * key blocks are the scale blocks (``scale_block`` keys); scores in log2
+        units: t = s * dq_i * dk_j * log2(e) / sqrt(d) (/ d if rotated), where s
+        is the exact dot product of the decoded codes;
+      * a reference max m is kept per query; it moves to a block's max only
+        when that max exceeds m by more than ``tau``; with tau = 0 this is the
+        sketch's running max (m_new = max(m, rowmax));
+      * P entering the product with V is e4m3(2^(t - m) * r_j) with
+        r_j = dv_j / dv_ref, dv_ref the largest V descale among the key blocks
+        that the query's block can see (all blocks when not causal); so P <= 2^tau;
+      * the old partial output is multiplied by 2^(m_old - m_new) when m moves
+        (the sketch's exp(old max - new max));
+      * l sums the unquantised 2^(t - m); O = dv_ref * O_acc / l;
+        LSE = ln 2 * (m + log2 l), the natural log-sum-exp of the scaled scores;
+      * O is delivered in BF16 ([P1] "How it gets verified": BF16 output),
+        rounded to nearest even (``bf16_output``); LSE stays float64.
+    Arithmetic is float64 apart from the e4m3 rounding of P and the final BF16
+    rounding of O.  With ``quantize_p=False, bf16_output=False`` the result
+    equals E1 up to float64 rounding.
+    """
+    q = e4m3.decode(q8)
+    k = e4m3.decode(k8)
+    v = e4m3.decode(v8)
+    qd = np.asarray(q_descale, dtype=np.float64)
+    kd = np.asarray(k_descale, dtype=np.float64)
+    vd = np.asarray(v_descale, dtype=np.float64)
+    n, d = q.shape[-2], q.shape[-1]
+    lead = q.shape[:-2]
+    score_scale = math.log2(math.e) / math.sqrt(d) / (d if hadamard else 1)
+    row_idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    nb = -(-n // scale_block)
+    o_all = np.empty(lead + (len(row_idx), d))
+    lse_all = np.empty(lead + (len(row_idx),))
+    for idx in np.ndindex(*lead):
+        qh, kh, vh = q[idx][row_idx], k[idx], v[idx]
+        qdr = qd[idx][row_idx // scale_block]
+        own_blk = row_idx // scale_block
+        if causal:
+            dv_ref = np.array([vd[idx][:b + 1].max() for b in own_blk])
+        else:
+            dv_ref = np.full(len(row_idx), vd[idx].max())
+        m = np.full(len(row_idx), -np.inf)
+        l = np.zeros(len(row_idx))
+        acc = np.zeros((len(row_idx), d))
+        for j in range(nb):
+            k0, k1 = j * scale_block, min(n, (j + 1) * scale_block)
+            s = qh @ kh[k0:k1].T
+            t = s * (qdr * kd[idx][j] * score_scale)[:, None]
+            if causal:
+                t = np.where(np.arange(k0, k1)[None, :] <= row_idx[:, None], t, -np.inf)
+            tmax = t.max(axis=1)
+            upd = tmax > m + tau
+            m_new = np.where(upd, tmax, m)
+            alpha = np.where(upd, np.exp2(np.where(np.isfinite(m), m - m_new, -np.inf)), 1.0)
+            m = m_new
+            ok = np.isfinite(m)
+            pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
+            pu[~ok] = 0.0
+            r = vd[idx][j] / dv_ref
+            pq = pu * r[:, None]
+            if quantize_p:
+                pq = e4m3.decode(e4m3.encode(pq))
+            l = alpha * l + pu.sum(axis=1)
+            acc = alpha[:, None] * acc + pq @ vh[k0:k1]
+        o_all[idx] = acc * dv_ref[:, None] / l[:, None]
+        lse_all[idx] = math.log(2.0) * (m + np.log2(l))
+    if bf16_output:
+        o_all = round_to_bf16(o_all)
+    return o_all, lse_all
+
+
+def round_to_bf16(x):
+    """Nearest bfloat16 value (ties to even) of each float64, returned as float64.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range; the value is
+    rounded once from float64 (no intermediate float32 rounding).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, fexp = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(fexp - 1, -126)
+    quantum = np.ldexp(1.0, e - 7)
+    return np.copysign(np.rint(a / quantum) * quantum, x)

@@ -1,0 +1,168 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+* quantize_qkv_fp8: codes and descales bit-exact against the oracle's float32
+  emulation (oracle.quantize).
+* attn_fp8_fwd: O and LSE against exact FP64 attention of the dequantised
+  inputs (oracle.emulated_fp8_attention), within RMSE 2e-3 and max-abs
+  2e-2 + half a BF16 ulp; LSE within 2e-3 * max(1, |LSE|).
+* attn_bf16_fwd: against exact FP64 attention of the BF16-rounded inputs.
+
+Small shapes are checked in full; they span several tiles and a ragged tail.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_attention_forward_amd as fa
+import workloads
+from oracle import attention as oatt
+from oracle import quantize as oq
+from tests.gpu_common import (bf16_round, check_fp8_output, dev, gpu_quantize, host, rms)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+QUANT_CASES = [
+    # B, H, N, D, scale_block, hadamard, seed, kind
+    (1, 2, 256, 64, 64, True, 0x5EED, "iid"),
+    (2, 3, 300, 128, 128, True, 7, "outlier"),
+    (1, 2, 200, 128, 64, False, 1, "iid"),
+    (1, 1, 65, 64, 128, True, 2 ** 64 - 1, "iid"),
+    (2, 2, 1, 128, 128, True, 3, "iid"),
+    (1, 4, 513, 128, 128, True, 0x5EED, "channel"),
+    (1, 2, 130, 64, 64, False, 9, "outlier"),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}".format(*c[:6]))
+def test_quantize_bit_exact(case):
+    B, H, N, D, sb, had, seed, kind = case
+    q, k, v = workloads.generate(kind, B, H, N, D, 100 + N)
+    got = [host(t) for t in gpu_quantize(q, k, v, sb, had, seed)]
+    ref = oq.quantize_qkv(q, k, v, sb, had, seed)
+    names = ("q8", "k8", "v8", "q_descale", "k_descale", "v_descale")
+    for g, r, nm in zip(got, ref, names):
+        assert g.shape == r.shape, nm
+        if g.dtype == np.uint8:
+            bad = np.count_nonzero(g != r)
+            assert bad == 0, f"{nm}: {bad} codes differ"
+        else:
+            assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), f"{nm}: descales differ"
+
+
+def test_quantize_zero_and_extreme_blocks():
+    B, H, N, D, sb = 1, 2, 256, 128, 128
+    q, k, v = workloads.generate("iid", B, H, N, D, 5)
+    v[0, 0, :128] = 0.0                      # an all-zero block: descale 1, zero codes
+    v[0, 0, 128:200] = -0.0
+    q[0, 1, 5, 7] = 3.0e4                    # a huge outlier
+    k[0, 1, 130:, :] *= 1e-30                # tiny values: subnormal e4m3 codes
+    got = [host(t) for t in gpu_quantize(q, k, v, sb, True, 11)]
+    ref = oq.quantize_qkv(q, k, v, sb, True, 11)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g.view(np.uint8) if g.dtype == np.uint8 else g.view(np.uint32),
+                              r.view(np.uint8) if r.dtype == np.uint8 else r.view(np.uint32))
+
+
+ATTN_CASES = [
+    # B, H, N, D, scale_block, hadamard, causal, kind
+    (1, 2, 256, 64, 64, True, False, "iid"),
+    (1, 2, 256, 64, 64, True, True, "iid"),
+    (2, 2, 300, 128, 128, True, False, "outlier"),
+    (2, 2, 300, 128, 128, True, True, "outlier"),
+    (1, 2, 1000, 128, 64, True, True, "iid"),
+    (1, 1, 1, 128, 128, True, False, "iid"),
+    (1, 1, 1, 64, 64, False, True, "iid"),
+    (1, 2, 129, 64, 128, False, False, "iid"),
+    (1, 3, 700, 128, 128, False, True, "channel"),
+    (1, 2, 640, 128, 128, True, True, "channel"),
+]
+
+
+def _fp8_run(q, k, v, sb, had, causal, seed=0x5EED):
+    q8, k8, v8, qd, kd, vd = gpu_quantize(q, k, v, sb, had, seed)
+    o, lse = fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=sb, hadamard=had, causal=causal)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}".format(*c[:7]))
+def test_attn_fp8_matches_emulated_fp8(case):
+    B, H, N, D, sb, had, causal, kind = case
+    q, k, v = workloads.generate(kind, B, H, N, D, 200 + N)
+    o, lse = _fp8_run(q, k, v, sb, had, causal)
+    qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED)
+    # the same pipeline emulated (P re-quantised to e4m3 as the kernel does)
+    o2, l2 = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal)
+    if kind == "channel" and not had:
+        # unrotated channel outliers: FP8 MFMA group accumulation error in S
+        # dominates (see LOOSE in test_gpu_workloads)
+        r2, m2 = rms(o - o2), float(np.max(np.abs(o - o2)))
+        assert r2 <= 2e-2 and np.all(np.abs(lse - l2) <= 2e-2 * np.maximum(1.0, np.abs(l2)))
+    else:
+        r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " vs E2")
+        # what is left is the BF16 rounding of O, the FP8 accumulation of the
+        # matrix cores and rare flips of a P rounding
+        assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
+    o1, l1 = oatt.emulated_fp8_attention(*qq, sb, had, causal)
+    r1 = rms(o - o1)
+    print(f"{case}: RMSE vs E2 {r2:.3e} (max {m2:.3e}); vs E1 {r1:.3e}; RMS(O) {rms(o1):.3e}")
+
+
+BF16_CASES = [
+    (1, 2, 256, 64, False), (1, 2, 256, 64, True), (2, 2, 300, 128, False), (2, 2, 300, 128, True),
+    (1, 1, 1, 128, True), (1, 2, 1000, 128, True), (1, 1, 65, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "B{}H{}N{}D{}c{}".format(*c))
+def test_attn_bf16_matches_reference(case):
+    B, H, N, D, causal = case
+    q, k, v = workloads.generate("iid", B, H, N, D, 300 + N)
+    qb, kb, vb = (bf16_round(x) for x in (q, k, v))
+    to16 = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    o, lse = fa.attn_bf16_fwd(to16(qb), to16(kb), to16(vb), causal=causal)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    o_ref, lse_ref = oatt.reference_attention(qb, kb, vb, causal)
+    err = np.abs(o - o_ref)
+    # P rounded to BF16 (relative 2^-9) inside the weighted sum moves O by at most
+    # 2^-9 max|V|; the result is rounded to BF16 (relative 2^-9); FP32 accumulation
+    # and the hardware exp2/log2 add far less.
+    vmax = np.abs(vb).max(axis=(-2, -1), keepdims=True)
+    assert np.all(err <= 2.0 ** -9 * vmax + 2.0 ** -8 * np.abs(o_ref) + 1e-6), float(err.max())
+    assert rms(o - o_ref) <= 2.0 ** -9 * (rms(o_ref) + rms(vb))
+    assert np.all(np.abs(lse - lse_ref) <= 1e-4 * np.maximum(1.0, np.abs(lse_ref)))
+
+
+def test_fp8_run_to_run_bitwise_deterministic():
+    q, k, v = workloads.generate("outlier", 1, 4, 1000, 128, 17)
+    o1, l1 = _fp8_run(q, k, v, 128, True, True)
+    o2, l2 = _fp8_run(q, k, v, 128, True, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+def test_fp8_causal_output_ignores_later_scale_blocks():
+    # block scales make O_i depend on later tokens of its own block only (never on later blocks)
+    q, k, v = workloads.generate("iid", 1, 2, 512, 128, 23)
+    o1, l1 = _fp8_run(q, k, v, 128, True, True)
+    k2, v2 = k.copy(), v.copy()
+    k2[..., 256:, :] *= 7.0
+    v2[..., 256:, :] *= -3.0
+    o2, l2 = _fp8_run(q, k2, v2, 128, True, True)
+    assert np.array_equal(o1[..., :256, :], o2[..., :256, :])
+    assert np.array_equal(l1[..., :256], l2[..., :256])
+
+
+def test_outputs_on_current_stream():
+    q, k, v = workloads.generate("iid", 1, 2, 256, 128, 29)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q8, k8, v8, qd, kd, vd = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=128)
+        o, lse = fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=128)
+    s.synchronize()
+    o_ref, _ = _fp8_run(q, k, v, 128, True, False)
+    assert np.array_equal(host(o), o_ref)

@@ -136,3 +136,88 @@ def test_emulated_attention_with_rotation_tracks_reference():
     o_bad, l_bad = attention.attention_fp64(quantize.dequantize(q8, qd, 64), quantize.dequantize(k8, kd, 64),
                                             quantize.dequantize(v8, vd, 64), False, 1 / math.sqrt(64))
     assert np.max(np.abs(l_bad - lr)) > 1.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tau", [0.0, 8.0])
+@pytest.mark.parametrize("had", [False, True])
+def test_tiled_fp8_loop_without_p_rounding_equals_e1(causal, tau, had):
+    shape = (1, 2, 300, 64)
+    q, k, v = (_rand(shape, s, 2.0).astype(np.float32) for s in (28, 29, 30))
+    v[0, 1, 128:192] *= 0.05                  # a V block with a much smaller scale
+    qq = quantize.quantize_qkv(q, k, v, 64, had, 0x5EED)
+    o1, l1 = attention.emulated_fp8_attention(*qq, 64, had, causal)
+    o2, l2 = attention.emulated_fp8_attention_tiled(*qq, 64, had, causal, tau=tau, quantize_p=False,
+                                                     bf16_output=False)
+    assert np.allclose(o2, o1, rtol=1e-11, atol=1e-13)
+    assert np.allclose(l2, l1, rtol=1e-12, atol=1e-13)
+    # rounding P moves O by e4m3's relative step at most, and never the LSE
+    o3, l3 = attention.emulated_fp8_attention_tiled(*qq, 64, had, causal, tau=tau, bf16_output=False)
+    assert np.allclose(l3, l1, rtol=1e-12, atol=1e-13)
+    vmax = np.abs(quantize.dequantize(qq[2], qq[5], 64)).max()
+    assert np.max(np.abs(o3 - o1)) <= 2.0 ** -4 * vmax
+    assert not np.array_equal(o3, o1)
+
+
+def test_tiled_fp8_loop_rows_subset():
+    shape = (1, 1, 200, 64)
+    q, k, v = (_rand(shape, s).astype(np.float32) for s in (31, 32, 33))
+    qq = quantize.quantize_qkv(q, k, v, 64, True, 1)
+    o, l = attention.emulated_fp8_attention_tiled(*qq, 64, True, True)
+    rows = [0, 63, 64, 199]
+    o2, l2 = attention.emulated_fp8_attention_tiled(*qq, 64, True, True, rows=rows)
+    assert np.array_equal(o[..., rows, :], o2) and np.array_equal(l[..., rows], l2)
+
+
+def test_tiled_fp8_loop_brute_force_tiny():
+    # two key blocks of 2 keys, d = 4: explicit loops with the stated P rule
+    from oracle import e4m3
+    rng = np.random.default_rng(34)
+    shape = (1, 1, 4, 4)
+    q, k, v = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
+    qq = quantize.quantize_qkv(q, k, v, 2, False, 0)
+    q8, k8, v8, qd, kd, vd = qq
+    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=0.0, bf16_output=False)
+    dq = e4m3.decode(q8)[0, 0]
+    dk = e4m3.decode(k8)[0, 0]
+    dv = e4m3.decode(v8)[0, 0]
+    c = math.log2(math.e) / 2.0
+    dvref = vd[0, 0].max()
+    for i in range(4):
+        t = [sum(dq[i, x] * dk[j, x] for x in range(4)) * qd[0, 0, i // 2] * kd[0, 0, j // 2] * c for j in range(4)]
+        m0 = max(t[0], t[1])
+        m1 = max(m0, t[2], t[3])
+        num = [0.0] * 4
+        for j in range(4):
+            mj = m0 if j < 2 else m1
+            pj = float(e4m3.decode(e4m3.encode(2.0 ** (t[j] - mj) * vd[0, 0, j // 2] / dvref)))
+            w = 2.0 ** (mj - m1)
+            for x in range(4):
+                num[x] += w * pj * dv[j, x]
+        l = sum(2.0 ** (tj - m1) for tj in t)
+        for x in range(4):
+            assert o[0, 0, i, x] == pytest.approx(num[x] * dvref / l, rel=1e-12, abs=1e-14)
+        assert lse[0, 0, i] == pytest.approx(math.log(2) * (m1 + math.log2(l)), rel=1e-12)
+
+
+def test_round_to_bf16_matches_torch():
+    import torch
+    rng = np.random.default_rng(35)
+    x = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.uniform(-30, 30, 100000),
+                        [0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -9, -(1.0 + 2.0 ** -8)]])
+    x = x.astype(np.float32).astype(np.float64)      # float32 values: one rounding on both sides
+    ours = attention.round_to_bf16(x)
+    ref = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    fin = np.abs(x) < 3e38
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.signbit(ours[-5]) and ours[-4] == 1.0
+    assert ours[-3] == 1.0 and ours[-2] == 1.0 + 2.0 ** -7 and ours[-1] == -1.0   # ties to even
+
+
+def test_tiled_fp8_loop_output_is_bf16_rounded():
+    shape = (1, 1, 128, 64)
+    q, k, v = (_rand(shape, s).astype(np.float32) for s in (36, 37, 38))
+    qq = quantize.quantize_qkv(q, k, v, 64, True, 2)
+    o_raw, l_raw = attention.emulated_fp8_attention_tiled(*qq, 64, True, False, bf16_output=False)
+    o, l = attention.emulated_fp8_attention_tiled(*qq, 64, True, False)
+    assert np.array_equal(o, attention.round_to_bf16(o_raw)) and np.array_equal(l, l_raw)
