@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and accuracy sample")
     ap.add_argument("--attn-only", action="store_true", help="time only attn_fp8_fwd launches (for profiling)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="with --attn-only: first run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -101,6 +103,13 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     if args.attn_only:
+        if args.copy_mb:
+            src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
         quant()
         for _ in range(args.warmup):
             attn()

@@ -10,7 +10,8 @@
 // LDS (the page rejects a separate global transpose for its bandwidth).
 // FLAMIA (4.3 Ablation Study) folds the score scales into one multiplier.
 //
-// gfx950 design (one workgroup = 4 waves = 128 queries of one head):
+// gfx950 design (one workgroup = 4 waves = 128 queries of one head; key
+// tiles of 64 keys):
 //   * S^T = K_j Q^T on v_mfma_f32_32x32x64_f8f6f4: A = K tile rows from LDS,
 //     B = the wave's 32 queries, held in registers for the whole loop.  In the
 //     accumulator each lane owns ONE query and 16 keys per 32-key subtile, so
@@ -21,15 +22,17 @@
 //     row-major V tile in LDS through ds_read_b64_tr_b8, in the key order the
 //     S accumulator produced.  O^T keeps one query per lane too, so the
 //     rescale factor is lane-local.
-//   * K_j / V_j tiles (BC keys = one scale block) stream into a two-slot LDS
-//     ring by direct global->LDS 16-byte loads, the next tile in flight while
-//     the current one is consumed; 16-byte columns are XOR-swizzled per row
-//     against LDS bank conflicts.
+//   * Software pipeline across tiles: the MFMAs of S_{j+1} are issued in the
+//     same basic block as the exponentials of tile j, so the matrix cores and
+//     the vector ALU work at the same time (the page's two-stage overlap of
+//     the score product of block j+1 with the softmax of block j, done here
+//     inside one wave).  K runs one tile ahead of V: two-slot LDS rings for K
+//     and for V, filled by direct global->LDS 16-byte loads one tile ahead of
+//     use; 16-byte columns are XOR-swizzled per row against bank conflicts.
 //   * Scale folding: t = s * (dq * dk_j * score_scale) in log2 units, one FMA
-//     per score with the running max; V's block scale dv_j enters as the
-//     factor r_j = dv_j / (max dv over the tiles the wave visits) inside the
-//     exponent (so P stays <= 256),
-//     and the row sum divides it back out.
+//     per score with the reference max; V's block scale dv_j enters as the
+//     factor r_j = dv_j / (max dv over the blocks the wave visits) inside the
+//     exponent (so P stays <= 256), and the row sum divides it back out.
 //   * Lazy rescale: the reference max only moves when a tile's max exceeds it
 //     by more than kTau (log2 units), so most tiles skip the O rescale; P is
 //     then <= 2^kTau, inside e4m3's range.
@@ -42,34 +45,42 @@
 namespace attnfp8 {
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units): P <= 2^8
+constexpr int kBC = kFp8KeyTile; // keys per tile
 
-template <int D, int BC>
+template <int D>
 struct Fp8Cfg {
   static constexpr int KSTEPS = D / 64;      // K-steps of the QK^T contraction
-  static constexpr int NSUB = BC / 32;       // 32-key subtiles of S^T
-  static constexpr int NKH = BC / 64;        // 64-key steps of the PV contraction
+  static constexpr int NSUB = kBC / 32;      // 32-key subtiles of S^T
   static constexpr int NDT = D / 32;         // 32-row (d) tiles of O^T
-  static constexpr int SLOTS = D / 16;       // 16-byte columns per row
-  static constexpr int TILE = BC * D;        // bytes per K or V tile
+  static constexpr int TILE = kBC * D;       // bytes per K or V tile
   static constexpr int CHUNKS = TILE / 1024; // 1 KiB direct-load chunks per tile
   static constexpr int CHUNKS_PER_WAVE = CHUNKS / kWaves;
   static_assert(CHUNKS % kWaves == 0, "tile must split evenly over the waves");
+  static_assert(kBC == 64, "one PV K-step per tile");
 };
 
-// XOR swizzles of the 16-byte column index, per LDS row
+// XOR swizzles of the 16-byte column index, per LDS row.  They depend on row
+// bits 0..3 only, so moving 16 rows (or more) is a constant address offset.
+//   K (ds_read_b128, one row per lane): any 16 consecutive rows at one logical
+//     column fall into distinct 16-byte bank groups.
+//   V (ds_read_b64_tr_b8): the 8 rows x 2 columns a 32-lane half reads fall
+//     into distinct bank groups.
 template <int D>
-__device__ __forceinline__ int swz_k(int row) { return row & (D / 16 - 1); }
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return (row & 7) ^ ((row >> 3) & 1);
+  else return ((row >> 1) ^ (row >> 2)) & 3;
+}
 template <int D>
 __device__ __forceinline__ int swz_v(int row) {
   if constexpr (D == 128) return (row & 3) | ((row >> 1) & 4);
-  else return row & 3;
+  else return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
-// Issue this wave's share of one K or V tile (rows kt*BC ..) into `buf`.
-template <int D, int BC, bool IS_V>
+// Issue this wave's share of one K or V tile (rows kt*kBC ..) into `buf`.
+template <int D, bool IS_V>
 __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ src, uint8_t* buf, int kt, int N,
                                           int wave, int lane) {
-  using C = Fp8Cfg<D, BC>;
+  using C = Fp8Cfg<D>;
 #pragma unroll
   for (int i = 0; i < C::CHUNKS_PER_WAVE; ++i) {
     const int c = wave * C::CHUNKS_PER_WAVE + i;
@@ -77,138 +88,188 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ src, uint8
     const int prow = pos / D;
     const int pslot = (pos % D) / 16;
     const int lslot = pslot ^ (IS_V ? swz_v<D>(prow) : swz_k<D>(prow));
-    int grow = kt * BC + prow;
+    int grow = kt * kBC + prow;
     grow = grow < N ? grow : N - 1;
     global_to_lds16(src + (size_t)grow * D + lslot * 16, buf + c * 1024);
   }
 }
 
-template <int D, int BC, bool CAUSAL>
-struct Fp8Tile {
-  using C = Fp8Cfg<D, BC>;
+// Per-lane LDS byte offsets of the MFMA operands inside one K / V tile; every
+// other operand of the tile is one of these plus a compile-time constant.
+template <int D>
+struct Fp8LaneOffsets {
+  using C = Fp8Cfg<D>;
+  int k[C::KSTEPS][2];   // K row (lane % 32), 16-byte halves of k-step ks; + sub * 32 * D
+  int v[C::NDT];         // V^T source row for d-tile dt; + 16 rr * D
 
-  // one key tile: S^T, softmax update, O^T += V^T P^T
-  static __device__ __forceinline__ void run(const uint8_t* kbuf, const uint8_t* vbuf, int kt, int N,
-                                             int lane, int iw, int my_q, const v8i (&qop)[C::KSTEPS],
-                                             float c_q, float dk, float inv_rv, float log2_rv,
-                                             v16f (&o)[C::NDT], float& m_ref, float& l_acc) {
+  __device__ __forceinline__ explicit Fp8LaneOffsets(int lane) {
     const int ql = lane & 31;
     const int h = lane >> 5;
-
-    // ---- S^T = K_j Q^T  (32 keys x 32 queries per subtile)
-    v16f s[C::NSUB];
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      const int row = sub * 32 + ql;
-      const uint8_t* rp = kbuf + row * D;
-      const int sw = swz_k<D>(row);
-      v16f acc = {};
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        const int s0 = 4 * ks + 2 * h;
-        v4i lo = lds_read_b128(rp + 16 * (s0 ^ sw));
-        v4i hi = lds_read_b128(rp + 16 * ((s0 + 1) ^ sw));
-        v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc = mfma_f8(a, qop[ks], acc);
-      }
-      s[sub] = acc;
-    }
-
-    // ---- masks (causal diagonal tiles, ragged last tile)
-    const int k0 = kt * BC;
-    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > iw);
-    if (need_mask) {
-      const int lim = CAUSAL ? (my_q < N - 1 ? my_q : N - 1) : N - 1;
-#pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > lim) s[sub][r] = -INFINITY;
-        }
-    }
-
-    // ---- tile max in log2 units (c > 0, so max commutes with the scale)
-    const float c = c_q * dk;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    float tmax = mx * c;
-    tmax = fmaxf(tmax, swap_halves(tmax));
-
-    // ---- lazy reference-max update
-    const bool upd = tmax > m_ref + kTau;
-    const float m_new = upd ? tmax : m_ref;
-    const float alpha = upd ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-    m_ref = m_new;
-
-    // ---- P = 2^(t - m + log2 r_j), row sum, e4m3 packing (B operand layout)
-    const float bias = log2_rv - m_ref;
-    float rs = 0.0f;
-    v8i pop[C::NKH];
-#pragma unroll
-    for (int kh = 0; kh < C::NKH; ++kh) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int sub = 2 * kh + s2;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 0], c, bias));
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 1], c, bias));
-          float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 2], c, bias));
-          float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 3], c, bias));
-          rs += (p0 + p1) + (p2 + p3);
-          int w = cvt_pk_fp8<false>(p0, p1, 0);
-          w = cvt_pk_fp8<true>(p2, p3, w);
-          pop[kh][4 * s2 + a] = w;
-        }
-      }
-    }
-    l_acc = alpha * l_acc + rs * inv_rv;
-
-    // ---- rescale O only when some lane moved its reference max
-    if (__builtin_amdgcn_ballot_w64(upd)) {
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-
-    // ---- O^T += V_j^T P^T ; V^T operand via transposing LDS reads
-    const int g = lane >> 4;          // 16-lane group
+      for (int half = 0; half < 2; ++half) k[ks][half] = ql * D + 16 * ((4 * ks + 2 * h + half) ^ swz_k<D>(ql));
+    // ds_read_b64_tr_b8 source lane i of 16-lane group g supplies key byte t = i / 2 of
+    // the (8 rr + t)-th operand byte; that key is row 8 (j / 4) + 4 h + j % 4, j = 8 rr + t
+    const int g = lane >> 4;
     const int i = lane & 15;
-    const int gh = g >> 1;            // k-chunk of this lane (== h)
-    const int gd = g & 1;             // which 16 d-rows of the 32
+    const int gh = g >> 1;
+    const int gd = g & 1;
+    const int row0 = 8 * (i >> 3) + 4 * gh + ((i >> 1) & 3);   // row for rr = 0
 #pragma unroll
-    for (int kh = 0; kh < C::NKH; ++kh) {
-      int rows[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int t = i >> 1;                          // key byte this source lane supplies
-        const int j = 8 * rr + t;                       // byte index in the 32-byte operand
-        rows[rr] = 64 * kh + 8 * (j >> 2) + 4 * gh + (j & 3);
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const int slot = 2 * dt + gd;
-        v2i part[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = rows[rr];
-          part[rr] = lds_read_tr8(vbuf + row * D + 16 * (slot ^ swz_v<D>(row)) + 8 * (i & 1));
-        }
-        v8i a = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
-        o[dt] = mfma_f8(a, pop[kh], o[dt]);
-      }
-    }
+    for (int dt = 0; dt < C::NDT; ++dt) v[dt] = row0 * D + 16 * ((2 * dt + gd) ^ swz_v<D>(row0)) + 8 * (i & 1);
   }
 };
 
-template <int D, int BC, bool CAUSAL>
+template <int D>
+using STile = v16f[Fp8Cfg<D>::NSUB];
+
+// K operands of one tile (A of S^T = K Q^T): 2 x 16 bytes per lane per MFMA
+template <int D>
+struct KOps {
+  v4i r[Fp8Cfg<D>::NSUB][Fp8Cfg<D>::KSTEPS][2];
+};
+
+template <int D>
+__device__ __forceinline__ void read_k(const uint8_t* kbuf, const Fp8LaneOffsets<D>& lo, KOps<D>& k) {
+  using C = Fp8Cfg<D>;
+#pragma unroll
+  for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) k.r[sub][ks][half] = lds_read_b128(kbuf + sub * 32 * D + lo.k[ks][half]);
+}
+
+template <int D>
+__device__ __forceinline__ v16f qk_mfma(const KOps<D>& k, const v8i (&qop)[Fp8Cfg<D>::KSTEPS], int sub) {
+  v16f acc = {};
+#pragma unroll
+  for (int ks = 0; ks < Fp8Cfg<D>::KSTEPS; ++ks) {
+    const v4i& a0 = k.r[sub][ks][0];
+    const v4i& a1 = k.r[sub][ks][1];
+    v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    acc = mfma_f8(a, qop[ks], acc);
+  }
+  return acc;
+}
+
+// S^T of one tile: 32 keys x 32 queries per subtile
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const Fp8LaneOffsets<D>& lo,
+                                        const v8i (&qop)[Fp8Cfg<D>::KSTEPS], STile<D>& s) {
+  KOps<D> k;
+  read_k<D>(kbuf, lo, k);
+#pragma unroll
+  for (int sub = 0; sub < Fp8Cfg<D>::NSUB; ++sub) s[sub] = qk_mfma<D>(k, qop, sub);
+}
+
+// Per-wave running state of the loop.
+template <int D>
+struct Fp8State {
+  v16f o[Fp8Cfg<D>::NDT];
+  float m_ref;     // reference max (log2 units)
+  float l_acc;     // this lane's half of the row sum
+  float alpha;     // rescale factor of the tile about to be accumulated
+  bool upd;        // this lane moved its reference max for that tile
+};
+
+// Mask + max + lazy reference update of a freshly computed score tile.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, int N, int lane, int iw, int my_q,
+                                           float c) {
+  using C = Fp8Cfg<D>;
+  const int h = lane >> 5;
+  const int k0 = t * kBC;
+  const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > iw);
+  if (need_mask) {
+    const int lim = (CAUSAL ? (my_q < N - 1 ? my_q : N - 1) : N - 1) - k0 - 4 * h;
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (sub * 32 + 8 * (r >> 2) + (r & 3) > lim) s[sub][r] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+  float tmax = mx * c;              // c > 0: the max commutes with the scale
+  tmax = fmaxf(tmax, swap_halves(tmax));
+  st.upd = tmax > st.m_ref + kTau;
+  const float m_new = st.upd ? tmax : st.m_ref;
+  st.alpha = st.upd ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
+  st.m_ref = m_new;
+}
+
+// One pipelined step.  On entry S_t (masked) and its statistics are ready and
+// K_{t+1} / V_t are resident.  Phase 1 issues the score MFMAs of tile t+1 in
+// the same block as the exponentials of tile t; phase 2 issues the P V MFMAs of
+// tile t in the same block as the statistics of tile t+1.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fp8_step(STile<D>& s, STile<D>& s_next, const uint8_t* knext, const uint8_t* vcur,
+                                         const Fp8LaneOffsets<D>& lo, const v8i (&qop)[Fp8Cfg<D>::KSTEPS],
+                                         Fp8State<D>& st, int t, int N, int lane, int iw, int my_q, float c,
+                                         float inv_rv, float log2_rv, float c_next, bool next_valid) {
+  using C = Fp8Cfg<D>;
+
+  // ---- rescale O when some lane moved its reference max for tile t
+  if (__builtin_amdgcn_ballot_w64(st.upd)) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[dt][r] *= st.alpha;
+  }
+
+  // ---- phase 1: S_{t+1} = K_{t+1} Q^T  ||  P_t = 2^(t - m + log2 r_t), row sum, e4m3
+  KOps<D> k;
+  read_k<D>(knext, lo, k);
+  const float bias = log2_rv - st.m_ref;
+  float rs = 0.0f;
+  v8i pop;
+#pragma unroll
+  for (int sub = 0; sub < C::NSUB; ++sub) {
+    s_next[sub] = qk_mfma<D>(k, qop, sub);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 0], c, bias));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 1], c, bias));
+      float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 2], c, bias));
+      float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 3], c, bias));
+      rs += (p0 + p1) + (p2 + p3);
+      int w = cvt_pk_fp8<false>(p0, p1, 0);
+      w = cvt_pk_fp8<true>(p2, p3, w);
+      pop[4 * sub + a] = w;
+    }
+  }
+  st.l_acc = st.alpha * st.l_acc + rs * inv_rv;
+#pragma unroll
+  for (int i = 0; i < C::NSUB * C::KSTEPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);   // then VALU work
+  }
+
+  // ---- phase 2: O^T += V_t^T P_t^T  ||  statistics of S_{t+1}
+  v2i part[C::NDT][4];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) part[dt][rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) {
+    v8i a = {part[dt][0][0], part[dt][0][1], part[dt][1][0], part[dt][1][1],
+             part[dt][2][0], part[dt][2][1], part[dt][3][0], part[dt][3][1]};
+    st.o[dt] = mfma_f8(a, pop, st.o[dt]);
+  }
+  // (a tile this wave will not visit must not move the reference max)
+  if (next_valid) tile_stats<D, CAUSAL>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
+}
+
+template <int D, int SB, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
-  using C = Fp8Cfg<D, BC>;
+  using C = Fp8Cfg<D>;
+  constexpr int TPB = SB / kBC;   // key tiles per scale block
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[C::TILE];
@@ -216,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -231,8 +292,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   const size_t head = (size_t)bh * N * D;
   const uint8_t* __restrict__ kh8 = p.k8 + head;
   const uint8_t* __restrict__ vh8 = p.v8 + head;
-  const float* kd = p.kd + (size_t)bh * p.nblk;
-  const float* vd = p.vd + (size_t)bh * p.nblk;
+  // block descales are read-only for the whole launch: scalar loads
+  const cfloat* kd = (const cfloat*)(p.kd + (size_t)bh * p.nblk);
+  const cfloat* vd = (const cfloat*)(p.vd + (size_t)bh * p.nblk);
 
   // queries of this lane as the B operand: Q[q][64ks + 32h .. +31]
   v8i qop[C::KSTEPS];
@@ -246,62 +308,76 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
       qop[ks] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
-  const int qblk = (my_q < N ? my_q : N - 1) / BC;
+  const int qblk = (my_q < N ? my_q : N - 1) / SB;
   const float c_q = p.qd[(size_t)bh * p.nblk + qblk] * p.score_scale;
 
-  const int n_kt = (N + BC - 1) / BC;
+  const int n_kt = (N + kBC - 1) / kBC;
   int n_kt_wg = n_kt;
   int kt_w = n_kt - 1;
   if (CAUSAL) {
     const int last_wg = (i0 + kQueryTile - 1 < N - 1) ? i0 + kQueryTile - 1 : N - 1;
-    n_kt_wg = last_wg / BC + 1;
+    n_kt_wg = last_wg / kBC + 1;
     const int last_w = (iw + kQueriesPerWave - 1 < N - 1) ? iw + kQueriesPerWave - 1 : N - 1;
-    kt_w = last_w / BC;
+    kt_w = last_w / kBC;
   }
 
-  // largest V block scale over the key tiles this wave visits (for causal calls
+  // largest V block scale over the key blocks this wave visits (for causal calls
   // only blocks up to the wave's own, so no output depends on a later block)
   float dvm = 0.0f;
-  for (int b = lane; b <= kt_w; b += 64) dvm = fmaxf(dvm, vd[b]);
+  for (int b = lane; b <= kt_w / TPB; b += 64) dvm = fmaxf(dvm, p.vd[(size_t)bh * p.nblk + b]);
   dvm = wave_max(dvm);
+  const float log2_dvm = __builtin_amdgcn_logf(dvm);
 
-  v16f o[C::NDT];
+  const Fp8LaneOffsets<D> lo(lane);
+  Fp8State<D> st;
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = (v16f){};
-  float m_ref = -1e30f;
-  float l_acc = 0.0f;
+  for (int dt = 0; dt < C::NDT; ++dt) st.o[dt] = (v16f){};
+  st.m_ref = -1e30f;
+  st.l_acc = 0.0f;
 
-  load_tile<D, BC, false>(kh8, kbuf0, 0, N, wave, lane);
-  load_tile<D, BC, true>(vh8, vbuf0, 0, N, wave, lane);
+  // per-tile constants: score scale c and V block ratio r = dv / dvm
+  auto c_of = [&](int t) { return c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
 
-  for (int kt = 0; kt < n_kt_wg; kt += 2) {
+  // prologue: K0, V0, K1 in flight; S_0 and its statistics
+  load_tile<D, false>(kh8, kbuf0, 0, N, wave, lane);
+  load_tile<D, true>(vh8, vbuf0, 0, N, wave, lane);
+  load_tile<D, false>(kh8, kbuf1, 1, N, wave, lane);
+  wait_vmem_all();
+  __syncthreads();
+  STile<D> sa, sb;
+  qk_tile<D>(kbuf0, lo, qop, sa);
+  st.alpha = 1.0f;
+  st.upd = false;
+  tile_stats<D, CAUSAL>(sa, st, 0, N, lane, iw, my_q, c_of(0));
+
+  // Step t (tiles of 64 keys): at its barrier K_{t+1} and V_t are resident; it
+  // prefetches K_{t+2} (into K_t's slot) and V_{t+1} (into V_{t-1}'s slot).
+  for (int t = 0; t < n_kt_wg; t += 2) {
     wait_vmem_all();
     __syncthreads();
-    if (kt + 1 < n_kt_wg) {
-      load_tile<D, BC, false>(kh8, kbuf1, kt + 1, N, wave, lane);
-      load_tile<D, BC, true>(vh8, vbuf1, kt + 1, N, wave, lane);
+    if (t + 2 < n_kt_wg) load_tile<D, false>(kh8, kbuf0, t + 2, N, wave, lane);
+    if (t + 1 < n_kt_wg) load_tile<D, true>(vh8, vbuf1, t + 1, N, wave, lane);
+    if (t <= kt_w) {
+      const float dv = vd[t / TPB];
+      fp8_step<D, CAUSAL>(sa, sb, kbuf1, vbuf0, lo, qop, st, t, N, lane, iw, my_q, c_of(t),
+                          dvm * __builtin_amdgcn_rcpf(dv), __builtin_amdgcn_logf(dv) - log2_dvm, c_of(t + 1),
+                          t + 1 <= kt_w);
     }
-    if (kt <= kt_w) {
-      const float dv = vd[kt];
-      Fp8Tile<D, BC, CAUSAL>::run(kbuf0, vbuf0, kt, N, lane, iw, my_q, qop, c_q, kd[kt], dvm / dv,
-                                  __builtin_amdgcn_logf(dv / dvm), o, m_ref, l_acc);
-    }
-    if (kt + 1 >= n_kt_wg) break;
+    if (t + 1 >= n_kt_wg) break;
     wait_vmem_all();
     __syncthreads();
-    if (kt + 2 < n_kt_wg) {
-      load_tile<D, BC, false>(kh8, kbuf0, kt + 2, N, wave, lane);
-      load_tile<D, BC, true>(vh8, vbuf0, kt + 2, N, wave, lane);
-    }
-    if (kt + 1 <= kt_w) {
-      const float dv = vd[kt + 1];
-      Fp8Tile<D, BC, CAUSAL>::run(kbuf1, vbuf1, kt + 1, N, lane, iw, my_q, qop, c_q, kd[kt + 1], dvm / dv,
-                                  __builtin_amdgcn_logf(dv / dvm), o, m_ref, l_acc);
+    if (t + 3 < n_kt_wg) load_tile<D, false>(kh8, kbuf1, t + 3, N, wave, lane);
+    if (t + 2 < n_kt_wg) load_tile<D, true>(vh8, vbuf0, t + 2, N, wave, lane);
+    if (t + 1 <= kt_w) {
+      const float dv = vd[(t + 1) / TPB];
+      fp8_step<D, CAUSAL>(sb, sa, kbuf0, vbuf1, lo, qop, st, t + 1, N, lane, iw, my_q, c_of(t + 1),
+                          dvm * __builtin_amdgcn_rcpf(dv), __builtin_amdgcn_logf(dv) - log2_dvm, c_of(t + 2),
+                          t + 2 <= kt_w);
     }
   }
 
   // ---- epilogue: O = dvm * O_acc / l ; LSE = ln 2 * (m + log2 l)
-  const float l_tot = l_acc + swap_halves(l_acc);
+  const float l_tot = st.l_acc + swap_halves(st.l_acc);
   const float inv_l = dvm / l_tot;
   if (my_q < N) {
     uint16_t* orow = p.o + head + (size_t)my_q * D;
@@ -310,15 +386,15 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d = 32 * dt + 8 * a + 4 * h;
-        uint32_t w0 = pack_bf16x2(o[dt][4 * a + 0] * inv_l, o[dt][4 * a + 1] * inv_l);
-        uint32_t w1 = pack_bf16x2(o[dt][4 * a + 2] * inv_l, o[dt][4 * a + 3] * inv_l);
+        uint32_t w0 = pack_bf16x2(st.o[dt][4 * a + 0] * inv_l, st.o[dt][4 * a + 1] * inv_l);
+        uint32_t w1 = pack_bf16x2(st.o[dt][4 * a + 2] * inv_l, st.o[dt][4 * a + 3] * inv_l);
         *(v2i*)(orow + d) = (v2i){(int)w0, (int)w1};
       }
-    if (h == 0) p.lse[(size_t)bh * N + my_q] = kLn2 * (m_ref + __builtin_amdgcn_logf(l_tot));
+    if (h == 0) p.lse[(size_t)bh * N + my_q] = kLn2 * (st.m_ref + __builtin_amdgcn_logf(l_tot));
   }
 }
 
-#define FP8_INST(D, BC, CA) template __global__ void attn_fp8_kernel<D, BC, CA>(AttnFp8Params);
+#define FP8_INST(D, SB, CA) template __global__ void attn_fp8_kernel<D, SB, CA>(AttnFp8Params);
 FP8_INST(64, 64, false)
 FP8_INST(64, 64, true)
 FP8_INST(64, 128, false)
@@ -328,10 +404,10 @@ FP8_INST(128, 64, true)
 FP8_INST(128, 128, false)
 FP8_INST(128, 128, true)
 
-template <int D, int BC>
+template <int D, int SB>
 static void launch_dc(const AttnFp8Params& p, int causal, dim3 grid, hipStream_t stream) {
-  if (causal) attn_fp8_kernel<D, BC, true><<<grid, 256, 0, stream>>>(p);
-  else attn_fp8_kernel<D, BC, false><<<grid, 256, 0, stream>>>(p);
+  if (causal) attn_fp8_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
+  else attn_fp8_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
 }
 
 hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int BH, hipStream_t stream) {

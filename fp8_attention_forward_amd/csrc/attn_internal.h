@@ -52,6 +52,7 @@ struct AttnBf16Params {
 constexpr int kWaves = 4;              // waves per workgroup in the attention kernels
 constexpr int kQueriesPerWave = 32;
 constexpr int kQueryTile = kWaves * kQueriesPerWave;
+constexpr int kFp8KeyTile = 64;      // keys per tile in the FP8 kernel
 
 hipError_t launch_quantize(const QuantParams& p, int D, int SB, int BH, hipStream_t stream);
 hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int BH, hipStream_t stream);

@@ -30,6 +30,10 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
+// read-only global data seen through the constant address space: uniform
+// indexing then compiles to scalar (s_load) reads
+typedef __attribute__((address_space(4))) const float cfloat;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

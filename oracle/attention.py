@@ -151,15 +151,17 @@ def brute_force_attention(q, k, v, causal, scale):
 
 
 def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
-                                 causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True):
+                                 causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True, block_c=64):
     """E2: the running-softmax loop over key blocks with P re-quantised to e4m3.
 
     The pages fix the loop (Implementation sketch) and that the matrix products
     run on 8-bit inputs; they are silent on the precision and scale of P.
     Reading taken here (the FP8 kernel follows it):
-      * key blocks are the scale blocks (``scale_block`` keys); scores in log2
+      * the loop visits key blocks of ``block_c`` keys (the sketch's block_c;
+        64 in the kernel), which must divide ``scale_block``; scores in log2
         units: t = s * dq_i * dk_j * log2(e) / sqrt(d) (/ d if rotated), where s
-        is the exact dot product of the decoded codes;
+        is the exact dot product of the decoded codes and dk_j the descale of
+        the scale block holding key block j;
       * a reference max m is kept per query; it moves to a block's max only
         when that max exceeds m by more than ``tau``; with tau = 0 this is the
         sketch's running max (m_new = max(m, rowmax));
@@ -186,7 +188,9 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     lead = q.shape[:-2]
     score_scale = math.log2(math.e) / math.sqrt(d) / (d if hadamard else 1)
     row_idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
-    nb = -(-n // scale_block)
+    if scale_block % block_c:
+        raise ValueError("block_c must divide scale_block")
+    nkb = -(-n // block_c)
     o_all = np.empty(lead + (len(row_idx), d))
     lse_all = np.empty(lead + (len(row_idx),))
     for idx in np.ndindex(*lead):
@@ -200,10 +204,11 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
         m = np.full(len(row_idx), -np.inf)
         l = np.zeros(len(row_idx))
         acc = np.zeros((len(row_idx), d))
-        for j in range(nb):
-            k0, k1 = j * scale_block, min(n, (j + 1) * scale_block)
+        for j in range(nkb):
+            k0, k1 = j * block_c, min(n, (j + 1) * block_c)
+            sb = k0 // scale_block
             s = qh @ kh[k0:k1].T
-            t = s * (qdr * kd[idx][j] * score_scale)[:, None]
+            t = s * (qdr * kd[idx][sb] * score_scale)[:, None]
             if causal:
                 t = np.where(np.arange(k0, k1)[None, :] <= row_idx[:, None], t, -np.inf)
             tmax = t.max(axis=1)
@@ -214,7 +219,7 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
             ok = np.isfinite(m)
             pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
             pu[~ok] = 0.0
-            r = vd[idx][j] / dv_ref
+            r = vd[idx][sb] / dv_ref
             pq = pu * r[:, None]
             if quantize_p:
                 pq = e4m3.decode(e4m3.encode(pq))

@@ -177,7 +177,8 @@ def test_tiled_fp8_loop_brute_force_tiny():
     q, k, v = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
     qq = quantize.quantize_qkv(q, k, v, 2, False, 0)
     q8, k8, v8, qd, kd, vd = qq
-    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=0.0, bf16_output=False)
+    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=0.0, bf16_output=False,
+                                                     block_c=2)
     dq = e4m3.decode(q8)[0, 0]
     dk = e4m3.decode(k8)[0, 0]
     dv = e4m3.decode(v8)[0, 0]
@@ -221,3 +222,16 @@ def test_tiled_fp8_loop_output_is_bf16_rounded():
     o_raw, l_raw = attention.emulated_fp8_attention_tiled(*qq, 64, True, False, bf16_output=False)
     o, l = attention.emulated_fp8_attention_tiled(*qq, 64, True, False)
     assert np.array_equal(o, attention.round_to_bf16(o_raw)) and np.array_equal(l, l_raw)
+
+
+def test_tiled_fp8_loop_block_size_only_moves_p_rounding():
+    shape = (1, 2, 300, 64)
+    q, k, v = (_rand(shape, s).astype(np.float32) for s in (39, 40, 41))
+    qq = quantize.quantize_qkv(q, k, v, 128, True, 3)
+    o1, l1 = attention.emulated_fp8_attention(*qq, 128, True, True)
+    kw = dict(quantize_p=False, bf16_output=False)
+    for bc in (32, 64, 128):
+        o, l = attention.emulated_fp8_attention_tiled(*qq, 128, True, True, block_c=bc, **kw)
+        assert np.allclose(o, o1, rtol=1e-11, atol=1e-13) and np.allclose(l, l1, rtol=1e-12)
+    with pytest.raises(ValueError):
+        attention.emulated_fp8_attention_tiled(*qq, 128, True, True, block_c=48)
