@@ -270,10 +270,13 @@ template <int D, int SB, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   using C = Fp8Cfg<D>;
   constexpr int TPB = SB / kBC;   // key tiles per scale block
+  // three-slot rings for K and V: tiles arrive two steps after their loads are issued
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf2[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf2[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -339,42 +342,49 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   auto c_of = [&](int t) { return c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
 
   // prologue: K0, V0, K1 in flight; S_0 and its statistics
+  // prologue: K0, K1, V0 resident; K2, V1 in flight; S_0 and its statistics
   load_tile<D, false>(kh8, kbuf0, 0, N, wave, lane);
-  load_tile<D, true>(vh8, vbuf0, 0, N, wave, lane);
   load_tile<D, false>(kh8, kbuf1, 1, N, wave, lane);
+  load_tile<D, true>(vh8, vbuf0, 0, N, wave, lane);
   wait_vmem_all();
   __syncthreads();
+  load_tile<D, false>(kh8, kbuf2, 2, N, wave, lane);
+  load_tile<D, true>(vh8, vbuf1, 1, N, wave, lane);
   STile<D> sa, sb;
   qk_tile<D>(kbuf0, lo, qop, sa);
   st.alpha = 1.0f;
   st.upd = false;
   tile_stats<D, CAUSAL>(sa, st, 0, N, lane, iw, my_q, c_of(0));
 
-  // Step t (tiles of 64 keys): at its barrier K_{t+1} and V_t are resident; it
-  // prefetches K_{t+2} (into K_t's slot) and V_{t+1} (into V_{t-1}'s slot).
-  for (int t = 0; t < n_kt_wg; t += 2) {
-    wait_vmem_all();
-    __syncthreads();
-    if (t + 2 < n_kt_wg) load_tile<D, false>(kh8, kbuf0, t + 2, N, wave, lane);
-    if (t + 1 < n_kt_wg) load_tile<D, true>(vh8, vbuf1, t + 1, N, wave, lane);
-    if (t <= kt_w) {
-      const float dv = vd[t / TPB];
-      fp8_step<D, CAUSAL>(sa, sb, kbuf1, vbuf0, lo, qop, st, t, N, lane, iw, my_q, c_of(t),
-                          dvm * __builtin_amdgcn_rcpf(dv), __builtin_amdgcn_logf(dv) - log2_dvm, c_of(t + 1),
-                          t + 1 <= kt_w);
-    }
-    if (t + 1 >= n_kt_wg) break;
-    wait_vmem_all();
-    __syncthreads();
-    if (t + 3 < n_kt_wg) load_tile<D, false>(kh8, kbuf1, t + 3, N, wave, lane);
-    if (t + 2 < n_kt_wg) load_tile<D, true>(vh8, vbuf0, t + 2, N, wave, lane);
-    if (t + 1 <= kt_w) {
-      const float dv = vd[(t + 1) / TPB];
-      fp8_step<D, CAUSAL>(sb, sa, kbuf0, vbuf1, lo, qop, st, t + 1, N, lane, iw, my_q, c_of(t + 1),
-                          dvm * __builtin_amdgcn_rcpf(dv), __builtin_amdgcn_logf(dv) - log2_dvm, c_of(t + 2),
-                          t + 2 <= kt_w);
-    }
+  // Step t (tiles of 64 keys): K_{t+1} and V_t were issued two steps earlier;
+  // waiting until only the previous step's loads are outstanding, then a
+  // barrier, makes them resident for every wave.  The step then issues K_{t+3}
+  // (into K_t's slot) and V_{t+2} (into V_{t-1}'s slot); loads past the end
+  // re-read the last rows, so every step issues the same number of loads.
+#define FP8_STEP(I, KQ, KD, VP, VD, S1, S2)                                                           \
+  {                                                                                                  \
+    const int tt = t + (I);                                                                          \
+    if (tt >= n_kt_wg) break;                                                                        \
+    wait_vmem_prev_step<2 * C::CHUNKS_PER_WAVE>();                                                   \
+    workgroup_barrier();                                                                             \
+    load_tile<D, false>(kh8, KD, tt + 3, N, wave, lane);                                             \
+    load_tile<D, true>(vh8, VD, tt + 2, N, wave, lane);                                              \
+    if (tt <= kt_w) {                                                                                \
+      const float dv = vd[(tt < n_kt ? tt : n_kt - 1) / TPB];                                        \
+      fp8_step<D, CAUSAL>(S1, S2, KQ, VP, lo, qop, st, tt, N, lane, iw, my_q, c_of(tt),              \
+                          dvm * __builtin_amdgcn_rcpf(dv), __builtin_amdgcn_logf(dv) - log2_dvm,     \
+                          c_of(tt + 1), tt + 1 <= kt_w);                                             \
+    }                                                                                                \
   }
+  for (int t = 0; t < n_kt_wg; t += 6) {
+    FP8_STEP(0, kbuf1, kbuf0, vbuf0, vbuf2, sa, sb)
+    FP8_STEP(1, kbuf2, kbuf1, vbuf1, vbuf0, sb, sa)
+    FP8_STEP(2, kbuf0, kbuf2, vbuf2, vbuf1, sa, sb)
+    FP8_STEP(3, kbuf1, kbuf0, vbuf0, vbuf2, sb, sa)
+    FP8_STEP(4, kbuf2, kbuf1, vbuf1, vbuf0, sa, sb)
+    FP8_STEP(5, kbuf0, kbuf2, vbuf2, vbuf1, sb, sa)
+  }
+#undef FP8_STEP
 
   // ---- epilogue: O = dvm * O_acc / l ; LSE = ln 2 * (m + log2 l)
   const float l_tot = st.l_acc + swap_halves(st.l_acc);

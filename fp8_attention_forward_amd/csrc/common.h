@@ -72,6 +72,18 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Workgroup barrier without the memory fence of __syncthreads (which would wait
+// for every outstanding global load, including prefetches still in flight).
+// The LDS tiles a step reads were completed by an explicit vmcnt wait before it.
+__device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N): all but the N most recent vector-memory operations done
+template <int N>
+__device__ __forceinline__ void wait_vmem_prev_step() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // value of lane (l ^ 32)
 __device__ __forceinline__ float swap_halves(float x) {
   int lane = __lane_id();
