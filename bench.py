@@ -222,9 +222,9 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu):
     from oracle import attention as oatt
 
     cores = len(os.sched_getaffinity(0))
-    # whole heads (every query row), in a fixed order, until ~12 s of CPU time or 16 heads
+    # whole heads (every query row), in a fixed order, until ~12 s of CPU time or 64 heads
     order = [(b, h) for h in range(w.H) for b in range(w.B)]
-    order = order[::max(1, len(order) // 16)][:16]
+    order = order[::max(1, len(order) // 64)][:64]
     rows = np.arange(w.N)
     t0 = time.perf_counter()
     refs, heads = [], []
