@@ -26,9 +26,15 @@
 //     same basic block as the exponentials of tile j, so the matrix cores and
 //     the vector ALU work at the same time (the page's two-stage overlap of
 //     the score product of block j+1 with the softmax of block j, done here
-//     inside one wave).  K runs one tile ahead of V: two-slot LDS rings for K
-//     and for V, filled by direct global->LDS 16-byte loads one tile ahead of
-//     use; 16-byte columns are XOR-swizzled per row against bank conflicts.
+//     inside one wave).  K and V stream through three-slot LDS rings, two
+//     tiles ahead of use, by buffer loads that write LDS directly; all their
+//     address operands are scalar except one fixed per-lane offset, and rows
+//     past the end read as zeros.  16-byte columns are XOR-swizzled per row
+//     against bank conflicts.
+//   * Loop split: an unrolled main loop over the tiles that are complete and
+//     visible to every query of the workgroup (no mask code, ring slots as
+//     constants), then at most three tail steps for the diagonal and ragged
+//     tiles.
 //   * Scale folding: t = s * (dq * dk_j * score_scale) in log2 units, one FMA
 //     per score with the reference max; V's block scale dv_j enters as the
 //     factor r_j = dv_j / (max dv over the blocks the wave visits) inside the
@@ -46,6 +52,7 @@ namespace attnfp8 {
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units): P <= 2^8
 constexpr int kBC = kFp8KeyTile; // keys per tile
+constexpr int kRing = 3;         // LDS slots per operand ring
 
 template <int D>
 struct Fp8Cfg {
@@ -76,22 +83,42 @@ __device__ __forceinline__ int swz_v(int row) {
   else return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
-// Issue this wave's share of one K or V tile (rows kt*kBC ..) into `buf`.
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ src, uint8_t* buf, int kt, int N,
-                                          int wave, int lane) {
+// Per-lane constants of the tile loads: the buffer offset (inside one tile) of
+// each 16-byte piece this lane moves, already permuted by the LDS swizzle, and
+// the LDS address of the wave's first 1 KiB chunk in ring slot 0.
+template <int D>
+struct Fp8Dma {
   using C = Fp8Cfg<D>;
+  int koff[C::CHUNKS_PER_WAVE];
+  int voff[C::CHUNKS_PER_WAVE];
+  uint32_t lds0;
+
+  __device__ __forceinline__ Fp8Dma(int wave, int lane, uint32_t smem_addr) {
 #pragma unroll
-  for (int i = 0; i < C::CHUNKS_PER_WAVE; ++i) {
-    const int c = wave * C::CHUNKS_PER_WAVE + i;
-    const int pos = c * 1024 + lane * 16;
-    const int prow = pos / D;
-    const int pslot = (pos % D) / 16;
-    const int lslot = pslot ^ (IS_V ? swz_v<D>(prow) : swz_k<D>(prow));
-    int grow = kt * kBC + prow;
-    grow = grow < N ? grow : N - 1;
-    global_to_lds16(src + (size_t)grow * D + lslot * 16, buf + c * 1024);
+    for (int i = 0; i < C::CHUNKS_PER_WAVE; ++i) {
+      const int pos = (wave * C::CHUNKS_PER_WAVE + i) * 1024 + lane * 16;
+      const int prow = pos / D;
+      const int pslot = (pos % D) / 16;
+      koff[i] = prow * D + 16 * (pslot ^ swz_k<D>(prow));
+      voff[i] = prow * D + 16 * (pslot ^ swz_v<D>(prow));
+    }
+    lds0 = smem_addr + wave * C::CHUNKS_PER_WAVE * 1024;
   }
+};
+
+// Issue this wave's share of key tile kt (rows kt*kBC ..) of one head into the
+// LDS slot at byte offset slot_off.  Rows at or past `lim_bytes / D` read as
+// zeros, so every step issues the same number of loads.
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile(const uint8_t* head, uint32_t lim_bytes, int kt, uint32_t slot_off,
+                                           const Fp8Dma<D>& dma) {
+  using C = Fp8Cfg<D>;
+  const int off = kt * C::TILE;
+  const int rem = (int)lim_bytes - off;
+  const v4i rsrc = make_rsrc(head + off, (uint32_t)(rem > 0 ? rem : 0));
+#pragma unroll
+  for (int i = 0; i < C::CHUNKS_PER_WAVE; ++i)
+    buffer_to_lds16(rsrc, IS_V ? dma.voff[i] : dma.koff[i], dma.lds0 + slot_off + i * 1024);
 }
 
 // Per-lane LDS byte offsets of the MFMA operands inside one K / V tile; every
@@ -172,16 +199,19 @@ struct Fp8State {
   float l_acc;     // this lane's half of the row sum
   float alpha;     // rescale factor of the tile about to be accumulated
   bool upd;        // this lane moved its reference max for that tile
+  v8i pop;         // P^T of the last tile in e4m3 (B operand of the P V product)
 };
 
 // Mask + max + lazy reference update of a freshly computed score tile.
-template <int D, bool CAUSAL>
+// MASK = false: the tile is known to be complete and visible to every query
+// of the workgroup, and no mask code is emitted.
+template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, int N, int lane, int iw, int my_q,
                                            float c) {
   using C = Fp8Cfg<D>;
   const int h = lane >> 5;
   const int k0 = t * kBC;
-  const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > iw);
+  const bool need_mask = MASK && ((k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > iw));
   if (need_mask) {
     const int lim = (CAUSAL ? (my_q < N - 1 ? my_q : N - 1) : N - 1) - k0 - 4 * h;
 #pragma unroll
@@ -207,7 +237,7 @@ __device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, 
 // K_{t+1} / V_t are resident.  Phase 1 issues the score MFMAs of tile t+1 in
 // the same block as the exponentials of tile t; phase 2 issues the P V MFMAs of
 // tile t in the same block as the statistics of tile t+1.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK_NEXT>
 __device__ __forceinline__ void fp8_step(STile<D>& s, STile<D>& s_next, const uint8_t* knext, const uint8_t* vcur,
                                          const Fp8LaneOffsets<D>& lo, const v8i (&qop)[Fp8Cfg<D>::KSTEPS],
                                          Fp8State<D>& st, int t, int N, int lane, int iw, int my_q, float c,
@@ -227,7 +257,7 @@ __device__ __forceinline__ void fp8_step(STile<D>& s, STile<D>& s_next, const ui
   read_k<D>(knext, lo, k);
   const float bias = log2_rv - st.m_ref;
   float rs = 0.0f;
-  v8i pop;
+  v8i& pop = st.pop;
 #pragma unroll
   for (int sub = 0; sub < C::NSUB; ++sub) {
     s_next[sub] = qk_mfma<D>(k, qop, sub);
@@ -238,7 +268,9 @@ __device__ __forceinline__ void fp8_step(STile<D>& s, STile<D>& s_next, const ui
       float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 2], c, bias));
       float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 3], c, bias));
       rs += (p0 + p1) + (p2 + p3);
-      int w = cvt_pk_fp8<false>(p0, p1, 0);
+      // (the conversion keeps the other half of its destination: start from
+      // the previous tile's word, which is dead by now)
+      int w = cvt_pk_fp8<false>(p0, p1, pop[4 * sub + a]);
       w = cvt_pk_fp8<true>(p2, p3, w);
       pop[4 * sub + a] = w;
     }
@@ -263,20 +295,16 @@ __device__ __forceinline__ void fp8_step(STile<D>& s, STile<D>& s_next, const ui
     st.o[dt] = mfma_f8(a, pop, st.o[dt]);
   }
   // (a tile this wave will not visit must not move the reference max)
-  if (next_valid) tile_stats<D, CAUSAL>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
+  if (!MASK_NEXT || next_valid) tile_stats<D, CAUSAL, MASK_NEXT>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
 }
 
 template <int D, int SB, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   using C = Fp8Cfg<D>;
   constexpr int TPB = SB / kBC;   // key tiles per scale block
-  // three-slot rings for K and V: tiles arrive two steps after their loads are issued
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf2[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf2[C::TILE];
+  // three-slot rings for K (slots 0..2) and V (slots 3..5): a tile arrives two
+  // steps after its loads are issued
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kRing * C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -293,8 +321,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   const int h = lane >> 5;
 
   const size_t head = (size_t)bh * N * D;
-  const uint8_t* __restrict__ kh8 = p.k8 + head;
-  const uint8_t* __restrict__ vh8 = p.v8 + head;
+  const uint8_t* kh8 = p.k8 + head;
+  const uint8_t* vh8 = p.v8 + head;
   // block descales are read-only for the whole launch: scalar loads
   const cfloat* kd = (const cfloat*)(p.kd + (size_t)bh * p.nblk);
   const cfloat* vd = (const cfloat*)(p.vd + (size_t)bh * p.nblk);
@@ -315,14 +343,19 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   const float c_q = p.qd[(size_t)bh * p.nblk + qblk] * p.score_scale;
 
   const int n_kt = (N + kBC - 1) / kBC;
-  int n_kt_wg = n_kt;
-  int kt_w = n_kt - 1;
+  int n_kt_wg = n_kt;              // key tiles the workgroup steps through
+  int kt_w = n_kt - 1;             // last key tile this wave computes
+  int n_clean = N / kBC;           // leading tiles complete and visible to every query here
   if (CAUSAL) {
     const int last_wg = (i0 + kQueryTile - 1 < N - 1) ? i0 + kQueryTile - 1 : N - 1;
     n_kt_wg = last_wg / kBC + 1;
     const int last_w = (iw + kQueriesPerWave - 1 < N - 1) ? iw + kQueriesPerWave - 1 : N - 1;
     kt_w = last_w / kBC;
+    n_clean = n_clean < i0 / kBC ? n_clean : i0 / kBC;
   }
+  // bytes of K / V this workgroup reads; loads past them return zeros
+  const int rows_wg = N < n_kt_wg * kBC ? N : n_kt_wg * kBC;
+  const uint32_t lim = (uint32_t)rows_wg * D;
 
   // largest V block scale over the key blocks this wave visits (for causal calls
   // only blocks up to the wave's own, so no output depends on a later block)
@@ -332,59 +365,90 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   const float log2_dvm = __builtin_amdgcn_logf(dvm);
 
   const Fp8LaneOffsets<D> lo(lane);
+  const Fp8Dma<D> dma(wave, lane, lds_addr_of(smem));
   Fp8State<D> st;
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) st.o[dt] = (v16f){};
   st.m_ref = -1e30f;
   st.l_acc = 0.0f;
+  st.pop = (v8i){};
 
-  // per-tile constants: score scale c and V block ratio r = dv / dvm
+  // per-tile score scale
   auto c_of = [&](int t) { return c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
+  constexpr uint32_t KS = 0, VS = kRing * C::TILE;   // ring bases (byte offsets in smem)
 
-  // prologue: K0, V0, K1 in flight; S_0 and its statistics
   // prologue: K0, K1, V0 resident; K2, V1 in flight; S_0 and its statistics
-  load_tile<D, false>(kh8, kbuf0, 0, N, wave, lane);
-  load_tile<D, false>(kh8, kbuf1, 1, N, wave, lane);
-  load_tile<D, true>(vh8, vbuf0, 0, N, wave, lane);
+  issue_tile<D, false>(kh8, lim, 0, KS + 0 * C::TILE, dma);
+  issue_tile<D, false>(kh8, lim, 1, KS + 1 * C::TILE, dma);
+  issue_tile<D, true>(vh8, lim, 0, VS + 0 * C::TILE, dma);
   wait_vmem_all();
   __syncthreads();
-  load_tile<D, false>(kh8, kbuf2, 2, N, wave, lane);
-  load_tile<D, true>(vh8, vbuf1, 1, N, wave, lane);
+  issue_tile<D, false>(kh8, lim, 2, KS + 2 * C::TILE, dma);
+  issue_tile<D, true>(vh8, lim, 1, VS + 1 * C::TILE, dma);
   STile<D> sa, sb;
-  qk_tile<D>(kbuf0, lo, qop, sa);
+  qk_tile<D>(smem + KS, lo, qop, sa);
   st.alpha = 1.0f;
   st.upd = false;
-  tile_stats<D, CAUSAL>(sa, st, 0, N, lane, iw, my_q, c_of(0));
+  tile_stats<D, CAUSAL, true>(sa, st, 0, N, lane, iw, my_q, c_of(0));
 
-  // Step t (tiles of 64 keys): K_{t+1} and V_t were issued two steps earlier;
-  // waiting until only the previous step's loads are outstanding, then a
-  // barrier, makes them resident for every wave.  The step then issues K_{t+3}
-  // (into K_t's slot) and V_{t+2} (into V_{t-1}'s slot); loads past the end
-  // re-read the last rows, so every step issues the same number of loads.
-#define FP8_STEP(I, KQ, KD, VP, VD, S1, S2)                                                           \
+  // Step t: K_{t+1} and V_t were issued two steps earlier; waiting until only
+  // the previous step's loads are outstanding, then a barrier, makes them
+  // resident for every wave.  The step then issues K_{t+3} (into K_t's slot)
+  // and V_{t+2} (into V_{t-1}'s slot).  S_t lives in sa for even t.
+  //
+  // Main loop: steps whose next tile needs no mask and is computed by every
+  // wave; ring slots are compile-time constants (unrolled over 6 = 3 slots x
+  // 2 score buffers).
+  const int t_main = n_clean - 1;
+  int t = 0;
+#define FP8_MAIN(I, KN, KD, VC, VD, S1, S2)                                                            \
   {                                                                                                  \
     const int tt = t + (I);                                                                          \
-    if (tt >= n_kt_wg) break;                                                                        \
+    if (tt >= t_main) {                                                                              \
+      t = tt;                                                                                        \
+      break;                                                                                         \
+    }                                                                                                \
     wait_vmem_prev_step<2 * C::CHUNKS_PER_WAVE>();                                                   \
     workgroup_barrier();                                                                             \
-    load_tile<D, false>(kh8, KD, tt + 3, N, wave, lane);                                             \
-    load_tile<D, true>(vh8, VD, tt + 2, N, wave, lane);                                              \
-    if (tt <= kt_w) {                                                                                \
-      const float dv = vd[(tt < n_kt ? tt : n_kt - 1) / TPB];                                        \
-      fp8_step<D, CAUSAL>(S1, S2, KQ, VP, lo, qop, st, tt, N, lane, iw, my_q, c_of(tt),              \
-                          dvm * __builtin_amdgcn_rcpf(dv), __builtin_amdgcn_logf(dv) - log2_dvm,     \
-                          c_of(tt + 1), tt + 1 <= kt_w);                                             \
-    }                                                                                                \
+    issue_tile<D, false>(kh8, lim, tt + 3, KS + (KD) * C::TILE, dma);                                \
+    issue_tile<D, true>(vh8, lim, tt + 2, VS + (VD) * C::TILE, dma);                                 \
+    const float dv = vd[tt / TPB];                                                                   \
+    fp8_step<D, CAUSAL, false>(S1, S2, smem + KS + (KN) * C::TILE, smem + VS + (VC) * C::TILE, lo, qop, \
+                               st, tt, N, lane, iw, my_q, c_of(tt), dvm * __builtin_amdgcn_rcpf(dv),  \
+                               __builtin_amdgcn_logf(dv) - log2_dvm, c_of(tt + 1), true);            \
   }
-  for (int t = 0; t < n_kt_wg; t += 6) {
-    FP8_STEP(0, kbuf1, kbuf0, vbuf0, vbuf2, sa, sb)
-    FP8_STEP(1, kbuf2, kbuf1, vbuf1, vbuf0, sb, sa)
-    FP8_STEP(2, kbuf0, kbuf2, vbuf2, vbuf1, sa, sb)
-    FP8_STEP(3, kbuf1, kbuf0, vbuf0, vbuf2, sb, sa)
-    FP8_STEP(4, kbuf2, kbuf1, vbuf1, vbuf0, sa, sb)
-    FP8_STEP(5, kbuf0, kbuf2, vbuf2, vbuf1, sb, sa)
+  for (;; t += 6) {
+    FP8_MAIN(0, 1, 0, 0, 2, sa, sb)
+    FP8_MAIN(1, 2, 1, 1, 0, sb, sa)
+    FP8_MAIN(2, 0, 2, 2, 1, sa, sb)
+    FP8_MAIN(3, 1, 0, 0, 2, sb, sa)
+    FP8_MAIN(4, 2, 1, 1, 0, sa, sb)
+    FP8_MAIN(5, 0, 2, 2, 1, sb, sa)
   }
-#undef FP8_STEP
+#undef FP8_MAIN
+
+  // Tail (at most three steps): diagonal and ragged tiles, masks, and waves
+  // that stop early; ring slots computed at run time, S_t moved into sa.  The
+  // loads are waited for in full here (vmcnt(0)), so the wait stays correct
+  // whatever other memory operations the compiler schedules in this part.
+  if (t & 1) {
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) sa[sub] = sb[sub];
+  }
+  for (; t < n_kt_wg; ++t) {
+    wait_vmem_all();
+    workgroup_barrier();
+    issue_tile<D, false>(kh8, lim, t + 3, KS + (t % kRing) * C::TILE, dma);
+    issue_tile<D, true>(vh8, lim, t + 2, VS + ((t + 2) % kRing) * C::TILE, dma);
+    if (t <= kt_w) {
+      const float dv = vd[t / TPB];
+      fp8_step<D, CAUSAL, true>(sa, sb, smem + KS + ((t + 1) % kRing) * C::TILE, smem + VS + (t % kRing) * C::TILE,
+                                lo, qop, st, t, N, lane, iw, my_q, c_of(t), dvm * __builtin_amdgcn_rcpf(dv),
+                                __builtin_amdgcn_logf(dv) - log2_dvm, c_of(t + 1), t + 1 <= kt_w);
+#pragma unroll
+      for (int sub = 0; sub < C::NSUB; ++sub) sa[sub] = sb[sub];
+    }
+  }
 
   // ---- epilogue: O = dvm * O_acc / l ; LSE = ln 2 * (m + log2 l)
   const float l_tot = st.l_acc + swap_halves(st.l_acc);

@@ -67,6 +67,32 @@ __device__ __forceinline__ void global_to_lds16(const void* g, uint8_t* lds_base
   __builtin_amdgcn_global_load_lds(g, LDS_PTR(void, lds_base), 16, 0, 0);
 }
 
+// Buffer resource for raw byte access to [base, base + bytes): loads at or past
+// `bytes` return zeros without touching memory (gfx9 descriptor, 32-bit data
+// format, no stride, no swizzle).
+// The arguments must be wave-uniform; readfirstlane keeps the descriptor in
+// scalar registers whatever the compiler's divergence analysis concludes.
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return (v4i){__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes (buffer
+// offset voff) land at lds_addr + 16 * l.  Issued as inline assembly, so the
+// compiler neither counts it nor waits for it: the caller owns the vmcnt wait
+// and the barrier that make the data visible.  Every address operand is scalar
+// except the per-lane offset.
+__device__ __forceinline__ void buffer_to_lds16(const v4i& rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+
+// byte address of an LDS object as the hardware sees it
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)LDS_PTR(const uint8_t, p);
+}
+
 __device__ __forceinline__ void wait_vmem_all() {
   // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima
   __builtin_amdgcn_s_waitcnt(0x0F70);
