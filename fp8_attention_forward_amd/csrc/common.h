@@ -84,8 +84,16 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 // compiler neither counts it nor waits for it: the caller owns the vmcnt wait
 // and the barrier that make the data visible.  Every address operand is scalar
 // except the per-lane offset.
+//
+// The compiler's hazard checks do not look inside inline assembly, so the
+// statement brings its own wait states: on gfx9 a vector-memory instruction
+// that reads an SGPR written by a VALU instruction (v_readfirstlane, which
+// may well produce the descriptor) needs 5 wait states in between, and an LDS
+// DMA needs 1 after M0 is written.  s_nop 4 provides 5.
+#define ATTN_LDS_DMA_NOP "s_nop 4\n\t"
 __device__ __forceinline__ void buffer_to_lds16(const v4i& rsrc, int voff, uint32_t lds_addr) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+  asm volatile(ATTN_LDS_DMA_NOP "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
 }
 
 // byte address of an LDS object as the hardware sees it

@@ -1,0 +1,79 @@
+"""Invariants of the generated gfx950 code of the FP8 attention kernel (CPU only:
+hipcc cross-compiles the source to assembly).
+
+* Every tile / descale load that writes LDS directly is inline assembly that
+  the compiler's hazard checks do not see; each must carry its own wait states
+  (s_nop 4) so that a descriptor SGPR written by a VALU instruction, or M0, is
+  never read stale.
+* The unrolled main loop waits for its loads with a fixed vmcnt that counts
+  only those loads, so it must contain no vector-memory operation of the
+  compiler's own (scratch spills, global / flat accesses, buffer stores);
+  scalar loads are counted separately (lgkmcnt) and are allowed.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "fp8_attention_forward_amd", "csrc", "attn_fp8.hip")
+HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+
+pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-S", SRC, "-o", "-"]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-2000:]
+    parts = re.split(r"\n(?=_ZN7attnfp815attn_fp8_kernel\S*:)", res.stdout)
+    funcs = {}
+    for p in parts[1:]:
+        name = p.split(":", 1)[0]
+        funcs[name] = p.split("\n.Lfunc_end", 1)[0].splitlines()
+    assert len(funcs) == 8, sorted(funcs)
+    return funcs
+
+
+def _code(lines):
+    return [l.strip() for l in lines if l.strip() and not l.strip().startswith(";")]
+
+
+def test_every_lds_dma_carries_its_wait_states(kernels):
+    for name, lines in kernels.items():
+        code = _code(lines)
+        n = 0
+        for i, ins in enumerate(code):
+            if re.match(r"buffer_load_dword\S*\s.*\blds\b", ins):
+                n += 1
+                assert code[i - 1] == "s_nop 4", f"{name}: LDS DMA without its own wait states: {ins}"
+        assert n > 0, name
+
+
+def _loops(lines):
+    """(label, body lines) of every loop: from its header to its last back edge."""
+    out = []
+    for i, l in enumerate(lines):
+        if "Loop Header" in l:
+            lab = l.split(":", 1)[0]
+            back = [j for j, m in enumerate(lines) if re.search(r"s_c?branch\S*\s+" + re.escape(lab) + r"\s*$", m)]
+            out.append((lab, lines[i:max(back) + 1]))
+    return out
+
+
+def test_main_loop_has_no_compiler_memory_operations(kernels):
+    for name, lines in kernels.items():
+        loops = _loops(lines)
+        # the main loop is the one that issues the most tile loads
+        lab, body = max(loops, key=lambda lb: sum("offen lds" in l for l in lb[1]))
+        dma = sum("offen lds" in l for l in body)
+        assert dma >= 6 * 2, (name, lab, dma)   # six unrolled steps, a K and a V tile each
+        mem = [l.strip() for l in body if re.search(r"\b(scratch_|global_|flat_|buffer_store)", l)]
+        assert not mem, f"{name}: compiler vector-memory operations inside the main loop: {mem[:4]}"
+        waits = set(re.findall(r"vmcnt\((\d+)\)", "\n".join(body)))
+        assert len(waits) == 1, (name, waits)   # one fixed wait per step
