@@ -111,11 +111,13 @@ __device__ __forceinline__ void wait_vmem_all() {
 // The LDS tiles a step reads were completed by an explicit vmcnt wait before it.
 __device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// s_waitcnt vmcnt(N): all but the N most recent vector-memory operations done
+// s_waitcnt vmcnt(N): all but the N most recent vector-memory operations done.
+// Written as inline assembly so that it stays exactly where it is placed (the
+// compiler's own waits are added around it as needed).
 template <int N>
 __device__ __forceinline__ void wait_vmem_prev_step() {
   static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // value of lane (l ^ 32)

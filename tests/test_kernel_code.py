@@ -66,14 +66,30 @@ def _loops(lines):
     return out
 
 
-def test_main_loop_has_no_compiler_memory_operations(kernels):
+def _asm_blocks(lines):
+    """Instructions written as inline assembly (between the ASMSTART/ASMEND markers)."""
+    out, inside = [], False
+    for l in lines:
+        if "ASMSTART" in l:
+            inside = True
+        elif "ASMEND" in l:
+            inside = False
+        elif inside and l.strip():
+            out.append(l.strip())
+    return out
+
+
+def test_partial_tile_waits_count_only_tile_loads(kernels):
+    """A loop that waits for its tile loads with a partial vmcnt (the kernel's
+    own inline s_waitcnt) must not contain vector-memory operations of the
+    compiler's own, which that count does not include."""
     for name, lines in kernels.items():
-        loops = _loops(lines)
-        # the main loop is the one that issues the most tile loads
-        lab, body = max(loops, key=lambda lb: sum("offen lds" in l for l in lb[1]))
-        dma = sum("offen lds" in l for l in body)
-        assert dma >= 6 * 2, (name, lab, dma)   # six unrolled steps, a K and a V tile each
-        mem = [l.strip() for l in body if re.search(r"\b(scratch_|global_|flat_|buffer_store)", l)]
-        assert not mem, f"{name}: compiler vector-memory operations inside the main loop: {mem[:4]}"
-        waits = set(re.findall(r"vmcnt\((\d+)\)", "\n".join(body)))
-        assert len(waits) == 1, (name, waits)   # one fixed wait per step
+        n_partial = 0
+        for lab, body in _loops(lines):
+            mine = [w for w in _asm_blocks(body) if re.match(r"s_waitcnt vmcnt\((\d+)\)", w)]
+            if not any(int(re.search(r"\d+", w).group()) > 0 for w in mine):
+                continue
+            n_partial += 1
+            mem = [l.strip() for l in body if re.search(r"\b(scratch_|global_|flat_|buffer_store)", l)]
+            assert not mem, f"{name} {lab}: compiler vector-memory operations in a loop with partial waits: {mem[:4]}"
+        assert n_partial >= 1, name   # the main loop keeps loads in flight across steps
