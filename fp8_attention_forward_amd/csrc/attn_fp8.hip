@@ -233,28 +233,26 @@ __device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, 
   st.m_ref = m_new;
 }
 
-// One pipelined step.  On entry S_t (masked) and its statistics are ready and
-// K_{t+1} / V_t are resident.  Phase 1 issues the score MFMAs of tile t+1 in
-// the same block as the exponentials of tile t; phase 2 issues the P V MFMAs of
-// tile t in the same block as the statistics of tile t+1.
-template <int D, bool CAUSAL, bool MASK_NEXT>
-__device__ __forceinline__ void fp8_step(STile<D>& s, STile<D>& s_next, const uint8_t* knext, const uint8_t* vcur,
-                                         const Fp8LaneOffsets<D>& lo, const v8i (&qop)[Fp8Cfg<D>::KSTEPS],
-                                         Fp8State<D>& st, int t, int N, int lane, int iw, int my_q, float c,
-                                         float inv_rv, float log2_rv, float c_next, bool next_valid) {
+// One pipelined step in two phases with the workgroup barrier between them.
+// On entry S_t (masked) and its statistics are ready and the K operands of
+// tile t+1 are in registers (read from LDS during the previous step).
+// Phase 1 issues the score MFMAs of tile t+1 in the same block as the
+// exponentials of tile t.  Phase 2 (after the barrier) reads V_t and the K
+// operands of tile t+2 from LDS and issues the P V MFMAs of tile t in the same
+// block as the statistics of tile t+1.
+template <int D>
+__device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const KOps<D>& k,
+                                           const v8i (&qop)[Fp8Cfg<D>::KSTEPS], Fp8State<D>& st, float c,
+                                           float inv_rv, float log2_rv) {
   using C = Fp8Cfg<D>;
-
-  // ---- rescale O when some lane moved its reference max for tile t
+  // rescale O when some lane moved its reference max for tile t
   if (__builtin_amdgcn_ballot_w64(st.upd)) {
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[dt][r] *= st.alpha;
   }
-
-  // ---- phase 1: S_{t+1} = K_{t+1} Q^T  ||  P_t = 2^(t - m + log2 r_t), row sum, e4m3
-  KOps<D> k;
-  read_k<D>(knext, lo, k);
+  // S_{t+1} = K_{t+1} Q^T  ||  P_t = 2^(t - m + log2 r_t), row sum, e4m3
   const float bias = log2_rv - st.m_ref;
   float rs = 0.0f;
   v8i& pop = st.pop;
@@ -281,18 +279,26 @@ __device__ __forceinline__ void fp8_step(STile<D>& s, STile<D>& s_next, const ui
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);   // then VALU work
   }
+}
 
-  // ---- phase 2: O^T += V_t^T P_t^T  ||  statistics of S_{t+1}
+template <int D, bool CAUSAL, bool MASK_NEXT>
+__device__ __forceinline__ void fp8_phase2(STile<D>& s_next, const uint8_t* vcur, const uint8_t* knext2, KOps<D>& k,
+                                           const Fp8LaneOffsets<D>& lo, Fp8State<D>& st, int t, int N, int lane,
+                                           int iw, int my_q, float c_next, bool next_valid) {
+  using C = Fp8Cfg<D>;
+  // V_t^T operands first (the P V MFMAs wait for them), then the K operands
+  // of tile t+2 for the next step
   v2i part[C::NDT][4];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) part[dt][rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
+  read_k<D>(knext2, lo, k);
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) {
     v8i a = {part[dt][0][0], part[dt][0][1], part[dt][1][0], part[dt][1][1],
              part[dt][2][0], part[dt][2][1], part[dt][3][0], part[dt][3][1]};
-    st.o[dt] = mfma_f8(a, pop, st.o[dt]);
+    st.o[dt] = mfma_f8(a, st.pop, st.o[dt]);
   }
   // (a tile this wave will not visit must not move the reference max)
   if (!MASK_NEXT || next_valid) tile_stats<D, CAUSAL, MASK_NEXT>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
@@ -377,53 +383,61 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   auto c_of = [&](int t) { return c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
   constexpr uint32_t KS = 0, VS = kRing * C::TILE;   // ring bases (byte offsets in smem)
 
-  // prologue: K0, K1, V0 resident; K2, V1 in flight; S_0 and its statistics
+  // prologue: K0, K1, K2, V0 resident; S_0 and its statistics; K operands of
+  // tile 1 in registers; K3, V1 in flight (into K0's and a fresh V slot)
   issue_tile<D, false>(kh8, lim, 0, KS + 0 * C::TILE, dma);
   issue_tile<D, false>(kh8, lim, 1, KS + 1 * C::TILE, dma);
+  issue_tile<D, false>(kh8, lim, 2, KS + 2 * C::TILE, dma);
   issue_tile<D, true>(vh8, lim, 0, VS + 0 * C::TILE, dma);
   wait_vmem_all();
   __syncthreads();
-  issue_tile<D, false>(kh8, lim, 2, KS + 2 * C::TILE, dma);
-  issue_tile<D, true>(vh8, lim, 1, VS + 1 * C::TILE, dma);
   STile<D> sa, sb;
   qk_tile<D>(smem + KS, lo, qop, sa);
   st.alpha = 1.0f;
   st.upd = false;
   tile_stats<D, CAUSAL, true>(sa, st, 0, N, lane, iw, my_q, c_of(0));
+  KOps<D> kops;
+  read_k<D>(smem + KS + 1 * C::TILE, lo, kops);
+  __syncthreads();   // K0 and K1 read by every wave: K0's slot may be refilled
+  issue_tile<D, false>(kh8, lim, 3, KS + 0 * C::TILE, dma);
+  issue_tile<D, true>(vh8, lim, 1, VS + 1 * C::TILE, dma);
 
-  // Step t: K_{t+1} and V_t were issued two steps earlier; waiting until only
-  // the previous step's loads are outstanding, then a barrier, makes them
-  // resident for every wave.  The step then issues K_{t+3} (into K_t's slot)
-  // and V_{t+2} (into V_{t-1}'s slot).  S_t lives in sa for even t.
+  // Step t: phase 1 (S_{t+1} MFMAs with the K operands in registers, P_t),
+  // then wait until only the previous step's loads are outstanding and
+  // barrier: K_{t+2} and V_t (issued two steps earlier) are now resident for
+  // every wave, and every wave has finished reading K_{t+1} and V_{t-1}.  The
+  // step issues K_{t+4} (into K_{t+1}'s slot) and V_{t+2} (into V_{t-1}'s
+  // slot), then runs phase 2.  S_t lives in sa for even t.
   //
   // Main loop: steps whose next tile needs no mask and is computed by every
   // wave; ring slots are compile-time constants (unrolled over 6 = 3 slots x
   // 2 score buffers).
   const int t_main = n_clean - 1;
   int t = 0;
-#define FP8_MAIN(I, KN, KD, VC, VD, S1, S2)                                                            \
+#define FP8_MAIN(I, KR, KD, VC, VD, S1, S2)                                                            \
   {                                                                                                  \
     const int tt = t + (I);                                                                          \
     if (tt >= t_main) {                                                                              \
       t = tt;                                                                                        \
       break;                                                                                         \
     }                                                                                                \
+    const float dv = vd[tt / TPB];                                                                   \
+    fp8_phase1<D>(S1, S2, kops, qop, st, c_of(tt), dvm * __builtin_amdgcn_rcpf(dv),                  \
+                  __builtin_amdgcn_logf(dv) - log2_dvm);                                             \
     wait_vmem_prev_step<2 * C::CHUNKS_PER_WAVE>();                                                   \
     workgroup_barrier();                                                                             \
-    issue_tile<D, false>(kh8, lim, tt + 3, KS + (KD) * C::TILE, dma);                                \
+    issue_tile<D, false>(kh8, lim, tt + 4, KS + (KD) * C::TILE, dma);                                \
     issue_tile<D, true>(vh8, lim, tt + 2, VS + (VD) * C::TILE, dma);                                 \
-    const float dv = vd[tt / TPB];                                                                   \
-    fp8_step<D, CAUSAL, false>(S1, S2, smem + KS + (KN) * C::TILE, smem + VS + (VC) * C::TILE, lo, qop, \
-                               st, tt, N, lane, iw, my_q, c_of(tt), dvm * __builtin_amdgcn_rcpf(dv),  \
-                               __builtin_amdgcn_logf(dv) - log2_dvm, c_of(tt + 1), true);            \
+    fp8_phase2<D, CAUSAL, false>(S2, smem + VS + (VC) * C::TILE, smem + KS + (KR) * C::TILE, kops, lo, st, \
+                                 tt, N, lane, iw, my_q, c_of(tt + 1), true);                          \
   }
   for (;; t += 6) {
-    FP8_MAIN(0, 1, 0, 0, 2, sa, sb)
-    FP8_MAIN(1, 2, 1, 1, 0, sb, sa)
-    FP8_MAIN(2, 0, 2, 2, 1, sa, sb)
-    FP8_MAIN(3, 1, 0, 0, 2, sb, sa)
-    FP8_MAIN(4, 2, 1, 1, 0, sa, sb)
-    FP8_MAIN(5, 0, 2, 2, 1, sb, sa)
+    FP8_MAIN(0, 2, 1, 0, 2, sa, sb)
+    FP8_MAIN(1, 0, 2, 1, 0, sb, sa)
+    FP8_MAIN(2, 1, 0, 2, 1, sa, sb)
+    FP8_MAIN(3, 2, 1, 0, 2, sb, sa)
+    FP8_MAIN(4, 0, 2, 1, 0, sa, sb)
+    FP8_MAIN(5, 1, 0, 2, 1, sb, sa)
   }
 #undef FP8_MAIN
 
@@ -436,19 +450,24 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
     for (int sub = 0; sub < C::NSUB; ++sub) sa[sub] = sb[sub];
   }
   for (; t < n_kt_wg; ++t) {
+    const bool active = t <= kt_w;
+    if (active) {
+      const float dv = vd[t / TPB];
+      fp8_phase1<D>(sa, sb, kops, qop, st, c_of(t), dvm * __builtin_amdgcn_rcpf(dv),
+                    __builtin_amdgcn_logf(dv) - log2_dvm);
+    }
     wait_vmem_all();
     workgroup_barrier();
-    issue_tile<D, false>(kh8, lim, t + 3, KS + (t % kRing) * C::TILE, dma);
+    issue_tile<D, false>(kh8, lim, t + 4, KS + ((t + 1) % kRing) * C::TILE, dma);
     issue_tile<D, true>(vh8, lim, t + 2, VS + ((t + 2) % kRing) * C::TILE, dma);
-    if (t <= kt_w) {
-      const float dv = vd[t / TPB];
-      fp8_step<D, CAUSAL, true>(sa, sb, smem + KS + ((t + 1) % kRing) * C::TILE, smem + VS + (t % kRing) * C::TILE,
-                                lo, qop, st, t, N, lane, iw, my_q, c_of(t), dvm * __builtin_amdgcn_rcpf(dv),
-                                __builtin_amdgcn_logf(dv) - log2_dvm, c_of(t + 1), t + 1 <= kt_w);
+    if (active) {
+      fp8_phase2<D, CAUSAL, true>(sb, smem + VS + (t % kRing) * C::TILE, smem + KS + ((t + 2) % kRing) * C::TILE,
+                                  kops, lo, st, t, N, lane, iw, my_q, c_of(t + 1), t + 1 <= kt_w);
 #pragma unroll
       for (int sub = 0; sub < C::NSUB; ++sub) sa[sub] = sb[sub];
     }
   }
+  wait_vmem_all();   // no tile load may still be writing LDS when the workgroup ends
 
   // ---- epilogue: O = dvm * O_acc / l ; LSE = ln 2 * (m + log2 l)
   const float l_tot = st.l_acc + swap_halves(st.l_acc);
