@@ -6,7 +6,8 @@ One step = the whole FP8 path on one batch of synthetic input resident in HBM:
 quantize_qkv_fp8 (rotate + block-scale + e4m3) then attn_fp8_fwd.  `value` is
 algorithmic TFLOP/s of that step (4*D FLOP per visible query/key pair; causal
 pairs discounted), quantisation included.  The same run also reports the
-attention alone, the quantiser alone, the BF16 twin, the accuracy against the
+attention alone, the attention with Schraudolph exponentials (an option), the
+quantiser alone, the BF16 twin, the accuracy against the
 FP64 oracle on a bounded sample, the roofline of the attention kernel and the
 oracle's CPU throughput.  Prints ONE JSON line.
 """
@@ -171,9 +172,29 @@ def main():
     torch.cuda.synchronize()
     bf16_ms = bs.elapsed_time(be) / nbf
 
-    # fresh outputs of both paths for the accuracy sample
+    # ---- option: Schraudolph's bit-level exponential for the probabilities
+    o_sch = torch.empty_like(o)
+    l_sch = torch.empty_like(lse)
+
+    def attn_sch():
+        fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=sb, hadamard=w.hadamard, causal=w.causal,
+                        out=(o_sch, l_sch), exp2="schraudolph")
+
+    for _ in range(3):
+        attn_sch()
+    ss, se = ev(), ev()
+    nsch = max(10, args.steps // 4)
+    ss.record(stream)
+    for _ in range(nsch):
+        attn_sch()
+    se.record(stream)
+    torch.cuda.synchronize()
+    sch_ms = ss.elapsed_time(se) / nsch
+
+    # fresh outputs of the paths for the accuracy sample
     quant()
     attn()
+    attn_sch()
     torch.cuda.synchronize()
 
     attn_tflops = flops / (attn_avg * 1e-3) / 1e12
@@ -199,6 +220,9 @@ def main():
                       "frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4)},
         "quantiser": {"ms": round(quant_ms, 4), "gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                       "frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "exp2_schraudolph": {"tflops": round(flops / (sch_ms * 1e-3) / 1e12, 2), "ms": round(sch_ms, 4),
+                             "frac_fp8_peak": round(flops / (sch_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                             "note": "attention alone, probabilities by Schraudolph's bit-level exponential"},
         "bf16_twin": {"tflops": round(flops / (bf16_ms * 1e-3) / 1e12, 2), "ms": round(bf16_ms, 4),
                       "frac_bf16_peak": round(flops / (bf16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -209,12 +233,12 @@ def main():
     }
 
     if not args.no_cpu:
-        result.update(cpu_leg(w, q_np, k_np, v_np, o, ob))
+        result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch))
     print(json.dumps(result))
     return 0
 
 
-def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu):
+def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu):
     """Oracle leg: time the FP64 reference on a bounded sample of the workload on
     the host cores and use the same reference rows for the accuracy report."""
     import numpy as np
@@ -240,22 +264,26 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu):
     else:
         pairs = len(rows) * w.N
     cpu_flops = 4 * w.D * pairs * len(heads)
-    e8, e16, ref_all = [], [], []
+    e8, e16, es, ref_all = [], [], [], []
     for (b, h), (orf, _) in zip(heads, refs):
         g8 = o_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
         g16 = ob_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
+        gs = osch_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
         e8.append((g8 - orf[0, 0]).ravel())
         e16.append((g16 - orf[0, 0]).ravel())
+        es.append((gs - orf[0, 0]).ravel())
         ref_all.append(orf[0, 0].ravel())
-    e8, e16, ra = np.concatenate(e8), np.concatenate(e16), np.concatenate(ref_all)
+    e8, e16, es, ra = np.concatenate(e8), np.concatenate(e16), np.concatenate(es), np.concatenate(ref_all)
     rmse8 = float(np.sqrt(np.mean(e8 ** 2)))
     rmse16 = float(np.sqrt(np.mean(e16 ** 2)))
+    rmses = float(np.sqrt(np.mean(es ** 2)))
     cos = lambda e: float(np.dot(ra + e, ra) / (np.linalg.norm(ra + e) * np.linalg.norm(ra)))
     return {
         "accuracy": {"sample": f"{len(heads)} heads x {len(rows)} query rows vs FP64 exact attention",
                      "fp8_rmse": rmse8, "fp8_max_err": float(np.max(np.abs(e8))), "fp8_cosine": cos(e8),
                      "bf16_rmse": rmse16, "bf16_max_err": float(np.max(np.abs(e16))), "bf16_cosine": cos(e16),
                      "ratio_fp8_to_bf16_rmse": rmse8 / rmse16 if rmse16 > 0 else None,
+                     "fp8_schraudolph_rmse": rmses, "fp8_schraudolph_cosine": cos(es),
                      "bound_ratio": 2.0, "rms_o": float(np.sqrt(np.mean(ra ** 2)))},
         "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
                          "kind": "oracle",

@@ -8,6 +8,7 @@ is raised.
 
     q8, k8, v8, qd, kd, vd = quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED)
     o, lse = attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=128, hadamard=True, causal=False)
+    o, lse = attn_fp8_fwd(..., exp2="schraudolph")   # Schraudolph's bit-level exponential
     o16, lse16 = attn_bf16_fwd(qb, kb, vb, causal=False)
 """
 
@@ -19,11 +20,14 @@ import torch
 __all__ = [
     "LIB_PATH", "AttnError", "load_library", "quantize_qkv_fp8", "attn_fp8_fwd", "attn_bf16_fwd",
     "last_error", "abi_version", "EXPORTED_SYMBOLS", "ATTN_OK", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EHIP",
+    "ATTN_FP8_EXP2_SCHRAUDOLPH", "EXP2_MODES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_fp8.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
-EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "attn_fp8_fwd", "attn_bf16_fwd", "attn_fp8_last_error",
+ATTN_FP8_EXP2_SCHRAUDOLPH = 1
+EXP2_MODES = {"exact": 0, "schraudolph": ATTN_FP8_EXP2_SCHRAUDOLPH}
+EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "attn_fp8_fwd", "attn_fp8_fwd_opts", "attn_bf16_fwd", "attn_fp8_last_error",
                     "attn_fp8_abi_version")
 
 _lib = None
@@ -49,6 +53,9 @@ def load_library(path=None):
     lib.quantize_qkv_fp8.restype = i32
     lib.attn_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.attn_fp8_fwd.restype = i32
+    lib.attn_fp8_fwd_opts.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_uint,
+                                      vp, vp, vp]
+    lib.attn_fp8_fwd_opts.restype = i32
     lib.attn_bf16_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.attn_bf16_fwd.restype = i32
     lib.attn_fp8_last_error.argtypes = []
@@ -123,9 +130,15 @@ def quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED, out=N
 
 
 def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, hadamard=True,
-                 causal=False, out=None):
-    """FP8 attention forward; returns (o [B,H,N,D] bfloat16, lse [B,H,N] float32)."""
+                 causal=False, out=None, exp2="exact"):
+    """FP8 attention forward; returns (o [B,H,N,D] bfloat16, lse [B,H,N] float32).
+
+    exp2: "exact" (attn_fp8_fwd) or "schraudolph" (attn_fp8_fwd_opts with
+    ATTN_FP8_EXP2_SCHRAUDOLPH: bit-level exponentials for the probabilities).
+    """
     lib = load_library()
+    if exp2 not in EXP2_MODES:
+        raise ValueError(f"exp2 must be one of {sorted(EXP2_MODES)}")
     B, H, N, D = _shape4(q8, "q8")
     if _shape4(k8, "k8") != (B, H, N, D) or _shape4(v8, "v8") != (B, H, N, D):
         raise ValueError("q8, k8, v8 must have the same shape")
@@ -139,11 +152,15 @@ def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, h
     o, lse = out
     if _shape4(o, "o") != (B, H, N, D) or tuple(lse.shape) != (B, H, N):
         raise ValueError("o / lse have the wrong shape")
-    _check(lib.attn_fp8_fwd(
-        _ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
-        _ptr(q_descale, torch.float32, "q_descale"), _ptr(k_descale, torch.float32, "k_descale"),
-        _ptr(v_descale, torch.float32, "v_descale"), B, H, N, D, int(scale_block), int(bool(hadamard)),
-        int(bool(causal)), _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _stream(q8)))
+    args = (_ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
+            _ptr(q_descale, torch.float32, "q_descale"), _ptr(k_descale, torch.float32, "k_descale"),
+            _ptr(v_descale, torch.float32, "v_descale"), B, H, N, D, int(scale_block), int(bool(hadamard)),
+            int(bool(causal)))
+    tail = (_ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _stream(q8))
+    if exp2 == "exact":
+        _check(lib.attn_fp8_fwd(*args, *tail))
+    else:
+        _check(lib.attn_fp8_fwd_opts(*args, EXP2_MODES[exp2], *tail))
     return out
 
 

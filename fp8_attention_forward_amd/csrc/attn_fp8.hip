@@ -51,6 +51,44 @@
 namespace attnfp8 {
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units): P <= 2^8
+
+// Exponentials of the probabilities P.
+//   kExpExact: v_exp_f32 of the scaled score (one FMA + one transcendental).
+//   kExpSchraudolph: Schraudolph's approximation (N. N. Schraudolph, "A fast,
+//     compact approximation of the exponential function", Neural Computation
+//     11(4), 1999), in base 2 for float32: the bit pattern of 2^x is taken to
+//     be floor(2^23 (x + 127 - sigma)), i.e. floor(x) lands in the exponent
+//     field and the fractional part, linearly, in the mantissa; sigma =
+//     60801 / 2^20 is the paper's error-centring constant (relative error
+//     within -3.9% .. +2.0%).  One FMA builds 2^23 (x + 127 - sigma) straight
+//     from the raw score, one conversion (round toward zero, saturating:
+//     negative -> 0) makes the bits.  FLAMIA uses this approximation for
+//     inference (4.4 Bit-Level Exponentials at Inference).
+enum { kExpExact = 0, kExpSchraudolph = 1 };
+constexpr float kSchraudolphSigma = 60801.0f / 1048576.0f;
+
+template <int EXPM>
+struct ExpArgs {
+  float c, b;   // p = exp(s * c + b)
+  __device__ __forceinline__ ExpArgs(float c_log2, float bias_log2) {
+    if constexpr (EXPM == kExpExact) {
+      c = c_log2;
+      b = bias_log2;
+    } else {
+      c = c_log2 * 8388608.0f;
+      b = (bias_log2 + (127.0f - kSchraudolphSigma)) * 8388608.0f;
+    }
+  }
+  __device__ __forceinline__ float operator()(float s) const {
+    if constexpr (EXPM == kExpExact) {
+      return __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, b));
+    } else {
+      unsigned bits;
+      asm("v_cvt_u32_f32 %0, %1" : "=v"(bits) : "v"(__builtin_fmaf(s, c, b)));
+      return __builtin_bit_cast(float, bits);
+    }
+  }
+};
 constexpr int kBC = kFp8KeyTile; // keys per tile
 constexpr int kRing = 3;         // LDS slots per operand ring
 
@@ -240,7 +278,7 @@ __device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, 
 // exponentials of tile t.  Phase 2 (after the barrier) reads V_t and the K
 // operands of tile t+2 from LDS and issues the P V MFMAs of tile t in the same
 // block as the statistics of tile t+1.
-template <int D>
+template <int D, int EXPM>
 __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const KOps<D>& k,
                                            const v8i (&qop)[Fp8Cfg<D>::KSTEPS], Fp8State<D>& st, float c,
                                            float inv_rv, float log2_rv) {
@@ -253,7 +291,7 @@ __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const 
       for (int r = 0; r < 16; ++r) st.o[dt][r] *= st.alpha;
   }
   // S_{t+1} = K_{t+1} Q^T  ||  P_t = 2^(t - m + log2 r_t), row sum, e4m3
-  const float bias = log2_rv - st.m_ref;
+  const ExpArgs<EXPM> ex(c, log2_rv - st.m_ref);
   float rs = 0.0f;
   v8i& pop = st.pop;
 #pragma unroll
@@ -261,10 +299,10 @@ __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const 
     s_next[sub] = qk_mfma<D>(k, qop, sub);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 0], c, bias));
-      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 1], c, bias));
-      float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 2], c, bias));
-      float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][4 * a + 3], c, bias));
+      float p0 = ex(s[sub][4 * a + 0]);
+      float p1 = ex(s[sub][4 * a + 1]);
+      float p2 = ex(s[sub][4 * a + 2]);
+      float p3 = ex(s[sub][4 * a + 3]);
       rs += (p0 + p1) + (p2 + p3);
       // (the conversion keeps the other half of its destination: start from
       // the previous tile's word, which is dead by now)
@@ -304,7 +342,7 @@ __device__ __forceinline__ void fp8_phase2(STile<D>& s_next, const uint8_t* vcur
   if (!MASK_NEXT || next_valid) tile_stats<D, CAUSAL, MASK_NEXT>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
 }
 
-template <int D, int SB, bool CAUSAL>
+template <int D, int SB, bool CAUSAL, int EXPM>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   using C = Fp8Cfg<D>;
   constexpr int TPB = SB / kBC;   // key tiles per scale block
@@ -422,7 +460,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
       break;                                                                                         \
     }                                                                                                \
     const float dv = vd[tt / TPB];                                                                   \
-    fp8_phase1<D>(S1, S2, kops, qop, st, c_of(tt), dvm * __builtin_amdgcn_rcpf(dv),                  \
+    fp8_phase1<D, EXPM>(S1, S2, kops, qop, st, c_of(tt), dvm * __builtin_amdgcn_rcpf(dv),                  \
                   __builtin_amdgcn_logf(dv) - log2_dvm);                                             \
     wait_vmem_prev_step<2 * C::CHUNKS_PER_WAVE>();                                                   \
     workgroup_barrier();                                                                             \
@@ -453,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
     const bool active = t <= kt_w;
     if (active) {
       const float dv = vd[t / TPB];
-      fp8_phase1<D>(sa, sb, kops, qop, st, c_of(t), dvm * __builtin_amdgcn_rcpf(dv),
+      fp8_phase1<D, EXPM>(sa, sb, kops, qop, st, c_of(t), dvm * __builtin_amdgcn_rcpf(dv),
                     __builtin_amdgcn_logf(dv) - log2_dvm);
     }
     wait_vmem_all();
@@ -487,28 +525,36 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   }
 }
 
-#define FP8_INST(D, SB, CA) template __global__ void attn_fp8_kernel<D, SB, CA>(AttnFp8Params);
-FP8_INST(64, 64, false)
-FP8_INST(64, 64, true)
-FP8_INST(64, 128, false)
-FP8_INST(64, 128, true)
-FP8_INST(128, 64, false)
-FP8_INST(128, 64, true)
-FP8_INST(128, 128, false)
-FP8_INST(128, 128, true)
+#define FP8_INST(D, SB, CA, E) template __global__ void attn_fp8_kernel<D, SB, CA, E>(AttnFp8Params);
+#define FP8_INST_E(D, SB, CA) FP8_INST(D, SB, CA, kExpExact) FP8_INST(D, SB, CA, kExpSchraudolph)
+FP8_INST_E(64, 64, false)
+FP8_INST_E(64, 64, true)
+FP8_INST_E(64, 128, false)
+FP8_INST_E(64, 128, true)
+FP8_INST_E(128, 64, false)
+FP8_INST_E(128, 64, true)
+FP8_INST_E(128, 128, false)
+FP8_INST_E(128, 128, true)
 
-template <int D, int SB>
-static void launch_dc(const AttnFp8Params& p, int causal, dim3 grid, hipStream_t stream) {
-  if (causal) attn_fp8_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
-  else attn_fp8_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
+template <int D, int SB, int E>
+static void launch_dce(const AttnFp8Params& p, int causal, dim3 grid, hipStream_t stream) {
+  if (causal) attn_fp8_kernel<D, SB, true, E><<<grid, 256, 0, stream>>>(p);
+  else attn_fp8_kernel<D, SB, false, E><<<grid, 256, 0, stream>>>(p);
 }
 
-hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int BH, hipStream_t stream) {
+template <int D, int SB>
+static void launch_dc(const AttnFp8Params& p, int causal, int exp_mode, dim3 grid, hipStream_t stream) {
+  if (exp_mode == kExpSchraudolph) launch_dce<D, SB, kExpSchraudolph>(p, causal, grid, stream);
+  else launch_dce<D, SB, kExpExact>(p, causal, grid, stream);
+}
+
+hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int BH,
+                           hipStream_t stream) {
   dim3 grid(BH * p.n_qtiles);
-  if (D == 64 && SB == 64) launch_dc<64, 64>(p, causal, grid, stream);
-  else if (D == 64 && SB == 128) launch_dc<64, 128>(p, causal, grid, stream);
-  else if (D == 128 && SB == 64) launch_dc<128, 64>(p, causal, grid, stream);
-  else launch_dc<128, 128>(p, causal, grid, stream);
+  if (D == 64 && SB == 64) launch_dc<64, 64>(p, causal, exp_mode, grid, stream);
+  else if (D == 64 && SB == 128) launch_dc<64, 128>(p, causal, exp_mode, grid, stream);
+  else if (D == 128 && SB == 64) launch_dc<128, 64>(p, causal, exp_mode, grid, stream);
+  else launch_dc<128, 128>(p, causal, exp_mode, grid, stream);
   return hipGetLastError();
 }
 

@@ -55,7 +55,9 @@ constexpr int kQueryTile = kWaves * kQueriesPerWave;
 constexpr int kFp8KeyTile = 64;      // keys per tile in the FP8 kernel
 
 hipError_t launch_quantize(const QuantParams& p, int D, int SB, int BH, hipStream_t stream);
-hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int BH, hipStream_t stream);
+// exp_mode: 0 exact exponentials, 1 Schraudolph's bit-level approximation
+hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int BH,
+                           hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnBf16Params& p, int D, int causal, int BH, hipStream_t stream);
 
 }  // namespace attnfp8

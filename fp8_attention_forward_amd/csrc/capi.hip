@@ -52,6 +52,9 @@ int check_sizes(int B, int H, int N, int D) {
   const long long tiles = (long long)B * H * ((N + attnfp8::kQueryTile - 1) / attnfp8::kQueryTile);
   if (tiles >= (1LL << 31) || (long long)B * H >= (1LL << 31))
     return fail(ATTN_EINVAL, "B * H * ceil(N / %d) must be < 2^31", attnfp8::kQueryTile);
+  // per-head byte offsets (16-bit elements, plus the tiles loaded past the end) stay below 2^31
+  if ((long long)N * D * 2 >= (1LL << 31) - (1LL << 20))
+    return fail(ATTN_EINVAL, "N * D must be < 2^30 (got N = %d, D = %d)", N, D);
   return ATTN_OK;
 }
 
@@ -111,9 +114,10 @@ int quantize_qkv_fp8(const float* q, const float* k, const float* v, int B, int 
   return launched(attnfp8::launch_quantize(p, D, scale_block, B * H, (hipStream_t)stream), "quantize_qkv_fp8");
 }
 
-int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_descale,
-                 const float* k_descale, const float* v_descale, int B, int H, int N, int D, int scale_block,
-                 int hadamard, int causal, uint16_t* o_bf16, float* lse, void* stream) {
+int attn_fp8_fwd_opts(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_descale,
+                      const float* k_descale, const float* v_descale, int B, int H, int N, int D, int scale_block,
+                      int hadamard, int causal, unsigned flags, uint16_t* o_bf16, float* lse, void* stream) {
+  if (flags & ~(unsigned)ATTN_FP8_EXP2_SCHRAUDOLPH) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
   CHECK(check_sizes(B, H, N, D));
   CHECK(check_sb(scale_block));
   CHECK(check_ptr(q8, 16, "q8"));
@@ -135,8 +139,16 @@ int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const 
   double sc = 1.4426950408889634 / std::sqrt((double)D);
   if (hadamard) sc /= D;
   p.score_scale = (float)sc;
-  return launched(attnfp8::launch_attn_fp8(p, D, scale_block, causal ? 1 : 0, B * H, (hipStream_t)stream),
+  const int exp_mode = (flags & ATTN_FP8_EXP2_SCHRAUDOLPH) ? 1 : 0;
+  return launched(attnfp8::launch_attn_fp8(p, D, scale_block, causal ? 1 : 0, exp_mode, B * H, (hipStream_t)stream),
                   "attn_fp8_fwd");
+}
+
+int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_descale,
+                 const float* k_descale, const float* v_descale, int B, int H, int N, int D, int scale_block,
+                 int hadamard, int causal, uint16_t* o_bf16, float* lse, void* stream) {
+  return attn_fp8_fwd_opts(q8, k8, v8, q_descale, k_descale, v_descale, B, H, N, D, scale_block, hadamard, causal,
+                           0u, o_bf16, lse, stream);
 }
 
 int attn_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int H, int N, int D, int causal,

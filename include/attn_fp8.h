@@ -22,7 +22,8 @@
  *     of scales or sizes is made on the device path, so calls can be captured
  *     in a HIP graph.
  *   - Supported: D in {64, 128}; scale_block in {64, 128}; B, H, N >= 1;
- *     B * H * ceil(N / 128) < 2^31.  Only gfx950 devices are supported.
+ *     B * H * ceil(N / 128) < 2^31; N * D < 2^30.  Only gfx950 devices are
+ *     supported.
  *   - Return value: ATTN_OK, or an attn_status error.  On ATTN_EINVAL and
  *     ATTN_EUNSUPPORTED nothing is launched and no output is written.
  *     attn_fp8_last_error() then describes the error (per calling thread).
@@ -87,6 +88,26 @@ int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  int B, int H, int N, int D, int scale_block, int hadamard, int causal,
                  uint16_t* o_bf16, float* lse, void* stream);
 
+/* attn_fp8_fwd_opts -- attn_fp8_fwd with option flags (attn_fp8_fwd is this
+ * call with flags = 0).
+ *   flags             : ATTN_FP8_EXP2_SCHRAUDOLPH -> the probabilities use
+ *                       Schraudolph's bit-level exponential (N. N. Schraudolph,
+ *                       "A fast, compact approximation of the exponential
+ *                       function", Neural Computation 11(4), 1999) in base 2:
+ *                       the float32 bits of 2^x are floor(2^23 (x + 127 -
+ *                       60801/2^20)), saturated at 0 below; relative error
+ *                       -3.9% .. +2.0% per probability.  FLAMIA evaluates it
+ *                       for inference ("FLAMIA", 4.4 Bit-Level Exponentials at
+ *                       Inference).  The row sum uses the same approximated
+ *                       values; the O rescale factor stays exact.
+ *                       Any other bit -> ATTN_EINVAL.
+ */
+#define ATTN_FP8_EXP2_SCHRAUDOLPH 1u
+int attn_fp8_fwd_opts(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                      const float* q_descale, const float* k_descale, const float* v_descale,
+                      int B, int H, int N, int D, int scale_block, int hadamard, int causal,
+                      unsigned flags, uint16_t* o_bf16, float* lse, void* stream);
+
 /* attn_bf16_fwd -- the same loop on BF16 inputs (BF16 products, FP32
  * accumulation and statistics, P in BF16), no rotation or quantisation: the
  * 16-bit yardstick of the problem statement ("What is asked").
@@ -104,7 +125,7 @@ const char* attn_fp8_last_error(void);
 /* ABI version of this header (incremented on incompatible changes). */
 int attn_fp8_abi_version(void);
 
-#define ATTN_FP8_ABI_VERSION 1
+#define ATTN_FP8_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -32,13 +32,15 @@ Modules
              brute force, attention of the dequantised FP8 inputs (E1), and
              the block loop with P re-quantised to e4m3 (E2)
              [P2 Overview, Implementation sketch]
+  fastexp    Schraudolph's bit-level base-2 exponential (Neural Computation
+             11(4), 1999), the option of E2 [P3 4.4 Bit-Level Exponentials]
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` to something
 other than itself (closed forms, an independent library, brute force,
 invariants).  Unpinned parts are listed in the functions that have them.
 """
 
-from . import e4m3, philox, hadamard, quantize, attention  # noqa: F401
+from . import e4m3, philox, hadamard, quantize, attention, fastexp  # noqa: F401
 from .attention import (  # noqa: F401
     attention_fp64,
     reference_attention,

@@ -23,7 +23,7 @@ import math
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, fastexp
 from .quantize import dequantize
 
 
@@ -151,7 +151,8 @@ def brute_force_attention(q, k, v, causal, scale):
 
 
 def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
-                                 causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True, block_c=64):
+                                 causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True, block_c=64,
+                                 exp2="exact"):
     """E2: the running-softmax loop over key blocks with P re-quantised to e4m3.
 
     The pages fix the loop (Implementation sketch) and that the matrix products
@@ -177,7 +178,15 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     Arithmetic is float64 apart from the e4m3 rounding of P and the final BF16
     rounding of O.  With ``quantize_p=False, bf16_output=False`` the result
     equals E1 up to float64 rounding.
+
+    ``exp2="schraudolph"`` replaces the probabilities' exponential by
+    Schraudolph's bit-level approximation (``fastexp.schraudolph_exp2``), taken
+    of the whole exponent t - m + log2 r_j, as the kernel's option does:
+    P = e4m3(S(t - m + log2 r_j)) and l sums S(t - m + log2 r_j) / r_j.  The
+    rescale 2^(m_old - m_new) stays exact.
     """
+    if exp2 not in ("exact", "schraudolph"):
+        raise ValueError("exp2 must be 'exact' or 'schraudolph'")
     q = e4m3.decode(q8)
     k = e4m3.decode(k8)
     v = e4m3.decode(v8)
@@ -217,10 +226,15 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
             alpha = np.where(upd, np.exp2(np.where(np.isfinite(m), m - m_new, -np.inf)), 1.0)
             m = m_new
             ok = np.isfinite(m)
-            pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
-            pu[~ok] = 0.0
             r = vd[idx][sb] / dv_ref
-            pq = pu * r[:, None]
+            if exp2 == "exact":
+                pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
+                pu[~ok] = 0.0
+                pq = pu * r[:, None]
+            else:
+                pq = fastexp.schraudolph_exp2(t - np.where(ok, m, 0.0)[:, None] + np.log2(r)[:, None])
+                pq[~ok] = 0.0
+                pu = pq / r[:, None]
             if quantize_p:
                 pq = e4m3.decode(e4m3.encode(pq))
             l = alpha * l + pu.sum(axis=1)

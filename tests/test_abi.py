@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert fa.abi_version() == 1
+    assert fa.abi_version() == 2
     m = re.search(r"#define ATTN_FP8_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == fa.abi_version()
 
@@ -102,6 +102,21 @@ def test_quantize_rejects(lib, kw, frag):
 def test_attn_fp8_rejects(lib, kw, frag):
     assert _a(lib, **kw) == fa.ATTN_EINVAL
     assert frag in fa.last_error()
+
+
+def test_attn_fp8_opts_rejects_unknown_flags(lib):
+    args = [P, P, P, P, P, P, 1, 1, 64, 128, 128, 1, 0]
+    assert lib.attn_fp8_fwd_opts(*args, 2, P, P, None) == fa.ATTN_EINVAL
+    assert "unknown flags" in fa.last_error()
+    assert lib.attn_fp8_fwd_opts(*args, 1, NUL, P, None) == fa.ATTN_EINVAL   # valid flag, then validation
+    assert "o_bf16 is NULL" in fa.last_error()
+    m = re.search(r"#define ATTN_FP8_EXP2_SCHRAUDOLPH (\d+)u", open(HEADER).read())
+    assert int(m.group(1)) == fa.ATTN_FP8_EXP2_SCHRAUDOLPH
+
+
+def test_rejects_heads_too_long_for_32_bit_offsets(lib):
+    assert _a(lib, N=1 << 23, D=128) == fa.ATTN_EINVAL
+    assert "N * D" in fa.last_error()
 
 
 @pytest.mark.parametrize("kw,frag", [

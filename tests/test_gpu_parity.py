@@ -112,6 +112,28 @@ def test_attn_fp8_matches_emulated_fp8(case):
     print(f"{case}: RMSE vs E2 {r2:.3e} (max {m2:.3e}); vs E1 {r1:.3e}; RMS(O) {rms(o1):.3e}")
 
 
+# Schraudolph's bit-level exponential (attn_fp8_fwd_opts, ATTN_FP8_EXP2_SCHRAUDOLPH)
+# against E2 with the same approximation: the benchmark spec's tolerance again.
+EXP2_CASES = [c for c in ATTN_CASES if not (c[7] == "channel" and not c[5])]
+
+
+@pytest.mark.parametrize("case", EXP2_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}".format(*c[:7]))
+def test_attn_fp8_schraudolph_matches_emulation(case):
+    B, H, N, D, sb, had, causal, kind = case
+    q, k, v = workloads.generate(kind, B, H, N, D, 200 + N)
+    q8, k8, v8, qd, kd, vd = gpu_quantize(q, k, v, sb, had, 0x5EED)
+    o, lse = fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=sb, hadamard=had, causal=causal,
+                             exp2="schraudolph")
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED)
+    o2, l2 = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2="schraudolph")
+    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " schraudolph vs E2")
+    assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
+    oe, _ = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal)
+    print(f"{case}: schraudolph RMSE vs its E2 {r2:.3e} (max {m2:.3e}); vs exact-exp E2 {rms(o - oe):.3e}")
+
+
 BF16_CASES = [
     (1, 2, 256, 64, False), (1, 2, 256, 64, True), (2, 2, 300, 128, False), (2, 2, 300, 128, True),
     (1, 1, 1, 128, True), (1, 2, 1000, 128, True), (1, 1, 65, 64, False),

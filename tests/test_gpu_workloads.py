@@ -78,6 +78,29 @@ def test_workload_fp8_parity(name, cache):
               f"vs FP64 rmse {rms(og - orf):.3e}; RMS(O) {rms(orf):.3e}", flush=True)
 
 
+@pytest.mark.parametrize("name", ["outlier", "outlier_causal"])
+def test_workload_fp8_schraudolph_parity(name):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.generate_workload(w)
+    q8, k8, v8, qd, kd, vd = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=w.scale_block,
+                                                 hadamard=w.hadamard, seed=w.sign_seed)
+    o, lse = fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=w.scale_block, hadamard=w.hadamard,
+                             causal=w.causal, exp2="schraudolph")
+    torch.cuda.synchronize()
+    for (b, h) in _heads(w):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oq.quantize_qkv(q[sl], k[sl], v[sl], w.scale_block, w.hadamard, w.sign_seed)
+        rows = sample_rows(w.N, 24, seed=b * 1000 + h)
+        o2, l2 = oatt.emulated_fp8_attention_tiled(*ref, w.scale_block, w.hadamard, w.causal, rows=rows,
+                                                   exp2="schraudolph")
+        og = host(o[sl])[..., rows, :]
+        lg = host(lse[sl])[..., rows]
+        r2, m2 = check_fp8_output(og, lg, o2, l2, tag=f"{name} schraudolph head {(b, h)}")
+        orf, _ = oatt.reference_attention(q[sl], k[sl], v[sl], w.causal, rows=rows)
+        print(f"[{name} schraudolph] head {(b, h)}: vs E2 rmse {r2:.3e} max {m2:.3e}; vs FP64 rmse "
+              f"{rms(og - orf):.3e}", flush=True)
+
+
 @pytest.mark.parametrize("name", ["outlier", "outlier_causal", "ablation_tail"])
 def test_workload_bf16_parity(name):
     w = workloads.WORKLOADS[name]
