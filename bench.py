@@ -6,8 +6,8 @@ One step = the whole FP8 path on one batch of synthetic input resident in HBM:
 quantize_qkv_fp8 (rotate + block-scale + e4m3) then attn_fp8_fwd.  `value` is
 algorithmic TFLOP/s of that step (4*D FLOP per visible query/key pair; causal
 pairs discounted), quantisation included.  The same run also reports the
-attention alone, the attention with Schraudolph exponentials (an option), the
-quantiser alone, the BF16 twin, the accuracy against the
+attention alone, the attention options (Schraudolph exponentials; power-of-two
+block scales applied by the scaled MFMA), the quantiser alone, the BF16 twin, the accuracy against the
 FP64 oracle on a bounded sample, the roofline of the attention kernel and the
 oracle's CPU throughput.  Prints ONE JSON line.
 """
@@ -191,10 +191,35 @@ def main():
     torch.cuda.synchronize()
     sch_ms = ss.elapsed_time(se) / nsch
 
+    # ---- option: power-of-two (E8M0) block scales applied by the scaled MFMA
+    mx_out = tuple(torch.empty_like(x) for x in qout)
+    o_mx = torch.empty_like(o)
+    l_mx = torch.empty_like(lse)
+
+    def quant_mx():
+        fa.quantize_qkv_fp8(q, k, v, scale_block=sb, hadamard=w.hadamard, seed=w.sign_seed, out=mx_out, mx=True)
+
+    def attn_mx():
+        fa.attn_fp8_fwd(*mx_out, scale_block=sb, hadamard=w.hadamard, causal=w.causal, out=(o_mx, l_mx), mx=True)
+
+    quant_mx()
+    for _ in range(3):
+        attn_mx()
+    ms_, me_ = ev(), ev()
+    nmx = max(10, args.steps // 4)
+    ms_.record(stream)
+    for _ in range(nmx):
+        attn_mx()
+    me_.record(stream)
+    torch.cuda.synchronize()
+    mx_ms = ms_.elapsed_time(me_) / nmx
+
     # fresh outputs of the paths for the accuracy sample
     quant()
     attn()
     attn_sch()
+    quant_mx()
+    attn_mx()
     torch.cuda.synchronize()
 
     attn_tflops = flops / (attn_avg * 1e-3) / 1e12
@@ -223,6 +248,9 @@ def main():
         "exp2_schraudolph": {"tflops": round(flops / (sch_ms * 1e-3) / 1e12, 2), "ms": round(sch_ms, 4),
                              "frac_fp8_peak": round(flops / (sch_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                              "note": "attention alone, probabilities by Schraudolph's bit-level exponential"},
+        "mx_scales": {"tflops": round(flops / (mx_ms * 1e-3) / 1e12, 2), "ms": round(mx_ms, 4),
+                      "frac_fp8_peak": round(flops / (mx_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                      "note": "attention alone, power-of-two block scales applied by the scaled FP8 MFMA"},
         "bf16_twin": {"tflops": round(flops / (bf16_ms * 1e-3) / 1e12, 2), "ms": round(bf16_ms, 4),
                       "frac_bf16_peak": round(flops / (bf16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -233,12 +261,12 @@ def main():
     }
 
     if not args.no_cpu:
-        result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch))
+        result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch, o_mx))
     print(json.dumps(result))
     return 0
 
 
-def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu):
+def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu):
     """Oracle leg: time the FP64 reference on a bounded sample of the workload on
     the host cores and use the same reference rows for the accuracy report."""
     import numpy as np
@@ -264,7 +292,7 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu):
     else:
         pairs = len(rows) * w.N
     cpu_flops = 4 * w.D * pairs * len(heads)
-    e8, e16, es, ref_all = [], [], [], []
+    e8, e16, es, emx, ref_all = [], [], [], [], []
     for (b, h), (orf, _) in zip(heads, refs):
         g8 = o_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
         g16 = ob_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
@@ -272,8 +300,11 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu):
         e8.append((g8 - orf[0, 0]).ravel())
         e16.append((g16 - orf[0, 0]).ravel())
         es.append((gs - orf[0, 0]).ravel())
+        gm = omx_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
+        emx.append((gm - orf[0, 0]).ravel())
         ref_all.append(orf[0, 0].ravel())
     e8, e16, es, ra = np.concatenate(e8), np.concatenate(e16), np.concatenate(es), np.concatenate(ref_all)
+    emx = np.concatenate(emx)
     rmse8 = float(np.sqrt(np.mean(e8 ** 2)))
     rmse16 = float(np.sqrt(np.mean(e16 ** 2)))
     rmses = float(np.sqrt(np.mean(es ** 2)))
@@ -284,6 +315,7 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu):
                      "bf16_rmse": rmse16, "bf16_max_err": float(np.max(np.abs(e16))), "bf16_cosine": cos(e16),
                      "ratio_fp8_to_bf16_rmse": rmse8 / rmse16 if rmse16 > 0 else None,
                      "fp8_schraudolph_rmse": rmses, "fp8_schraudolph_cosine": cos(es),
+                     "fp8_mx_rmse": float(np.sqrt(np.mean(emx ** 2))), "fp8_mx_cosine": cos(emx),
                      "bound_ratio": 2.0, "rms_o": float(np.sqrt(np.mean(ra ** 2)))},
         "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
                          "kind": "oracle",

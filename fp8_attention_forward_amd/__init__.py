@@ -20,15 +20,16 @@ import torch
 __all__ = [
     "LIB_PATH", "AttnError", "load_library", "quantize_qkv_fp8", "attn_fp8_fwd", "attn_bf16_fwd",
     "last_error", "abi_version", "EXPORTED_SYMBOLS", "ATTN_OK", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EHIP",
-    "ATTN_FP8_EXP2_SCHRAUDOLPH", "EXP2_MODES",
+    "ATTN_FP8_EXP2_SCHRAUDOLPH", "ATTN_FP8_MX", "EXP2_MODES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_fp8.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_FP8_EXP2_SCHRAUDOLPH = 1
+ATTN_FP8_MX = 2
 EXP2_MODES = {"exact": 0, "schraudolph": ATTN_FP8_EXP2_SCHRAUDOLPH}
-EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "attn_fp8_fwd", "attn_fp8_fwd_opts", "attn_bf16_fwd", "attn_fp8_last_error",
-                    "attn_fp8_abi_version")
+EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "quantize_qkv_fp8_opts", "attn_fp8_fwd", "attn_fp8_fwd_opts", "attn_bf16_fwd",
+                    "attn_fp8_last_error", "attn_fp8_abi_version")
 
 _lib = None
 
@@ -51,6 +52,9 @@ def load_library(path=None):
     vp, i32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64
     lib.quantize_qkv_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, u64, vp, vp, vp, vp, vp, vp, vp]
     lib.quantize_qkv_fp8.restype = i32
+    lib.quantize_qkv_fp8_opts.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, u64, ctypes.c_uint,
+                                          vp, vp, vp, vp, vp, vp, vp]
+    lib.quantize_qkv_fp8_opts.restype = i32
     lib.attn_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.attn_fp8_fwd.restype = i32
     lib.attn_fp8_fwd_opts.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_uint,
@@ -102,8 +106,11 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED, out=None):
-    """Rotate (Q, K) + per-block scale + e4m3 encode; returns (q8, k8, v8, q_descale, k_descale, v_descale)."""
+def quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED, out=None, mx=False):
+    """Rotate (Q, K) + per-block scale + e4m3 encode; returns (q8, k8, v8, q_descale, k_descale, v_descale).
+
+    mx=True: power-of-two (E8M0) block scales (quantize_qkv_fp8_opts with ATTN_FP8_MX).
+    """
     lib = load_library()
     B, H, N, D = _shape4(q, "q")
     if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
@@ -120,21 +127,26 @@ def quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED, out=N
     for t, nm in ((qd, "q_descale"), (kd, "k_descale"), (vd, "v_descale")):
         if tuple(t.shape) != (B, H, nb):
             raise ValueError(f"{nm} must be [B, H, ceil(N/scale_block)]")
-    _check(lib.quantize_qkv_fp8(
-        _ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
-        B, H, N, D, int(scale_block), int(bool(hadamard)), int(seed) & 0xFFFFFFFFFFFFFFFF,
-        _ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
-        _ptr(qd, torch.float32, "q_descale"), _ptr(kd, torch.float32, "k_descale"),
-        _ptr(vd, torch.float32, "v_descale"), _stream(q)))
+    head = (_ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+            B, H, N, D, int(scale_block), int(bool(hadamard)), int(seed) & 0xFFFFFFFFFFFFFFFF)
+    tail = (_ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
+            _ptr(qd, torch.float32, "q_descale"), _ptr(kd, torch.float32, "k_descale"),
+            _ptr(vd, torch.float32, "v_descale"), _stream(q))
+    if mx:
+        _check(lib.quantize_qkv_fp8_opts(*head, ATTN_FP8_MX, *tail))
+    else:
+        _check(lib.quantize_qkv_fp8(*head, *tail))
     return out
 
 
 def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, hadamard=True,
-                 causal=False, out=None, exp2="exact"):
+                 causal=False, out=None, exp2="exact", mx=False):
     """FP8 attention forward; returns (o [B,H,N,D] bfloat16, lse [B,H,N] float32).
 
-    exp2: "exact" (attn_fp8_fwd) or "schraudolph" (attn_fp8_fwd_opts with
-    ATTN_FP8_EXP2_SCHRAUDOLPH: bit-level exponentials for the probabilities).
+    exp2: "exact" or "schraudolph" (ATTN_FP8_EXP2_SCHRAUDOLPH: bit-level
+    exponentials for the probabilities).  mx=True: power-of-two descales
+    applied by the matrix cores (ATTN_FP8_MX).  Any option goes through
+    attn_fp8_fwd_opts, none through attn_fp8_fwd.
     """
     lib = load_library()
     if exp2 not in EXP2_MODES:
@@ -157,10 +169,11 @@ def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, h
             _ptr(v_descale, torch.float32, "v_descale"), B, H, N, D, int(scale_block), int(bool(hadamard)),
             int(bool(causal)))
     tail = (_ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _stream(q8))
-    if exp2 == "exact":
+    flags = EXP2_MODES[exp2] | (ATTN_FP8_MX if mx else 0)
+    if flags == 0:
         _check(lib.attn_fp8_fwd(*args, *tail))
     else:
-        _check(lib.attn_fp8_fwd_opts(*args, EXP2_MODES[exp2], *tail))
+        _check(lib.attn_fp8_fwd_opts(*args, flags, *tail))
     return out
 
 

@@ -206,27 +206,40 @@ __device__ __forceinline__ void read_k(const uint8_t* kbuf, const Fp8LaneOffsets
       for (int half = 0; half < 2; ++half) k.r[sub][ks][half] = lds_read_b128(kbuf + sub * 32 * D + lo.k[ks][half]);
 }
 
-template <int D>
-__device__ __forceinline__ v16f qk_mfma(const KOps<D>& k, const v8i (&qop)[Fp8Cfg<D>::KSTEPS], int sub) {
+// FP8 MFMA; with MX the E8M0 exponents sa (per row of A) and sb (per column of
+// B) scale the products inside the matrix core (127 = 2^0).  Without MX the
+// unscaled instruction is used.
+template <bool MX>
+__device__ __forceinline__ v16f mfma_f8x(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  if constexpr (MX) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  else return mfma_f8(a, b, c);
+}
+
+// E8M0 exponent of a power-of-two float (2^-127 is the subnormal 0x00400000)
+__device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__builtin_bit_cast(uint32_t, pow2) >> 23) & 0xFF; }
+
+template <int D, bool MX>
+__device__ __forceinline__ v16f qk_mfma(const KOps<D>& k, const v8i (&qop)[Fp8Cfg<D>::KSTEPS], int sub, int sk,
+                                        int sq) {
   v16f acc = {};
 #pragma unroll
   for (int ks = 0; ks < Fp8Cfg<D>::KSTEPS; ++ks) {
     const v4i& a0 = k.r[sub][ks][0];
     const v4i& a1 = k.r[sub][ks][1];
     v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    acc = mfma_f8(a, qop[ks], acc);
+    acc = mfma_f8x<MX>(a, qop[ks], acc, sk, sq);
   }
   return acc;
 }
 
 // S^T of one tile: 32 keys x 32 queries per subtile
-template <int D>
+template <int D, bool MX>
 __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const Fp8LaneOffsets<D>& lo,
-                                        const v8i (&qop)[Fp8Cfg<D>::KSTEPS], STile<D>& s) {
+                                        const v8i (&qop)[Fp8Cfg<D>::KSTEPS], STile<D>& s, int sk, int sq) {
   KOps<D> k;
   read_k<D>(kbuf, lo, k);
 #pragma unroll
-  for (int sub = 0; sub < Fp8Cfg<D>::NSUB; ++sub) s[sub] = qk_mfma<D>(k, qop, sub);
+  for (int sub = 0; sub < Fp8Cfg<D>::NSUB; ++sub) s[sub] = qk_mfma<D, MX>(k, qop, sub, sk, sq);
 }
 
 // Per-wave running state of the loop.
@@ -278,10 +291,10 @@ __device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, 
 // exponentials of tile t.  Phase 2 (after the barrier) reads V_t and the K
 // operands of tile t+2 from LDS and issues the P V MFMAs of tile t in the same
 // block as the statistics of tile t+1.
-template <int D, int EXPM>
+template <int D, int EXPM, bool MX>
 __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const KOps<D>& k,
                                            const v8i (&qop)[Fp8Cfg<D>::KSTEPS], Fp8State<D>& st, float c,
-                                           float inv_rv, float log2_rv) {
+                                           float inv_rv, float log2_rv, int sk_next, int sq) {
   using C = Fp8Cfg<D>;
   // rescale O when some lane moved its reference max for tile t
   if (__builtin_amdgcn_ballot_w64(st.upd)) {
@@ -296,7 +309,7 @@ __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const 
   v8i& pop = st.pop;
 #pragma unroll
   for (int sub = 0; sub < C::NSUB; ++sub) {
-    s_next[sub] = qk_mfma<D>(k, qop, sub);
+    s_next[sub] = qk_mfma<D, MX>(k, qop, sub, sk_next, sq);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       float p0 = ex(s[sub][4 * a + 0]);
@@ -319,10 +332,10 @@ __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const 
   }
 }
 
-template <int D, bool CAUSAL, bool MASK_NEXT>
+template <int D, bool CAUSAL, bool MASK_NEXT, bool MX>
 __device__ __forceinline__ void fp8_phase2(STile<D>& s_next, const uint8_t* vcur, const uint8_t* knext2, KOps<D>& k,
                                            const Fp8LaneOffsets<D>& lo, Fp8State<D>& st, int t, int N, int lane,
-                                           int iw, int my_q, float c_next, bool next_valid) {
+                                           int iw, int my_q, float c_next, bool next_valid, int sv) {
   using C = Fp8Cfg<D>;
   // V_t^T operands first (the P V MFMAs wait for them), then the K operands
   // of tile t+2 for the next step
@@ -336,13 +349,13 @@ __device__ __forceinline__ void fp8_phase2(STile<D>& s_next, const uint8_t* vcur
   for (int dt = 0; dt < C::NDT; ++dt) {
     v8i a = {part[dt][0][0], part[dt][0][1], part[dt][1][0], part[dt][1][1],
              part[dt][2][0], part[dt][2][1], part[dt][3][0], part[dt][3][1]};
-    st.o[dt] = mfma_f8(a, st.pop, st.o[dt]);
+    st.o[dt] = mfma_f8x<MX>(a, st.pop, st.o[dt], sv, 127);
   }
   // (a tile this wave will not visit must not move the reference max)
   if (!MASK_NEXT || next_valid) tile_stats<D, CAUSAL, MASK_NEXT>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
 }
 
-template <int D, int SB, bool CAUSAL, int EXPM>
+template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   using C = Fp8Cfg<D>;
   constexpr int TPB = SB / kBC;   // key tiles per scale block
@@ -384,7 +397,11 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
     }
   }
   const int qblk = (my_q < N ? my_q : N - 1) / SB;
-  const float c_q = p.qd[(size_t)bh * p.nblk + qblk] * p.score_scale;
+  // MX: the matrix cores apply the power-of-two block scales (E8M0 exponents
+  // sq, sk, sv), so the score scale is the constant score_scale and V needs no
+  // fold into P
+  const float c_q = MX ? p.score_scale : p.qd[(size_t)bh * p.nblk + qblk] * p.score_scale;
+  const int sq = MX ? e8m0_of(p.qd[(size_t)bh * p.nblk + qblk]) : 0;
 
   const int n_kt = (N + kBC - 1) / kBC;
   int n_kt_wg = n_kt;              // key tiles the workgroup steps through
@@ -403,9 +420,12 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
 
   // largest V block scale over the key blocks this wave visits (for causal calls
   // only blocks up to the wave's own, so no output depends on a later block)
-  float dvm = 0.0f;
-  for (int b = lane; b <= kt_w / TPB; b += 64) dvm = fmaxf(dvm, p.vd[(size_t)bh * p.nblk + b]);
-  dvm = wave_max(dvm);
+  float dvm = 1.0f;
+  if constexpr (!MX) {
+    dvm = 0.0f;
+    for (int b = lane; b <= kt_w / TPB; b += 64) dvm = fmaxf(dvm, p.vd[(size_t)bh * p.nblk + b]);
+    dvm = wave_max(dvm);
+  }
   const float log2_dvm = __builtin_amdgcn_logf(dvm);
 
   const Fp8LaneOffsets<D> lo(lane);
@@ -418,7 +438,13 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   st.pop = (v8i){};
 
   // per-tile score scale
-  auto c_of = [&](int t) { return c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
+  auto c_of = [&](int t) { return MX ? c_q : c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
+  // E8M0 exponents of a tile's K and V block scales (MX only)
+  auto sk_of = [&](int t) { return MX ? e8m0_of(kd[(t < n_kt ? t : n_kt - 1) / TPB]) : 0; };
+  auto sv_of = [&](int t) { return MX ? e8m0_of(vd[(t < n_kt ? t : n_kt - 1) / TPB]) : 0; };
+  // factor 1/r and log2 r of a tile's V block (r = dv / dvm; 1 and 0 with MX)
+  auto ir_of = [&](float dv) { return MX ? 1.0f : dvm * __builtin_amdgcn_rcpf(dv); };
+  auto lr_of = [&](float dv) { return MX ? 0.0f : __builtin_amdgcn_logf(dv) - log2_dvm; };
   constexpr uint32_t KS = 0, VS = kRing * C::TILE;   // ring bases (byte offsets in smem)
 
   // prologue: K0, K1, K2, V0 resident; S_0 and its statistics; K operands of
@@ -430,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   wait_vmem_all();
   __syncthreads();
   STile<D> sa, sb;
-  qk_tile<D>(smem + KS, lo, qop, sa);
+  qk_tile<D, MX>(smem + KS, lo, qop, sa, sk_of(0), sq);
   st.alpha = 1.0f;
   st.upd = false;
   tile_stats<D, CAUSAL, true>(sa, st, 0, N, lane, iw, my_q, c_of(0));
@@ -460,14 +486,13 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
       break;                                                                                         \
     }                                                                                                \
     const float dv = vd[tt / TPB];                                                                   \
-    fp8_phase1<D, EXPM>(S1, S2, kops, qop, st, c_of(tt), dvm * __builtin_amdgcn_rcpf(dv),                  \
-                  __builtin_amdgcn_logf(dv) - log2_dvm);                                             \
+    fp8_phase1<D, EXPM, MX>(S1, S2, kops, qop, st, c_of(tt), ir_of(dv), lr_of(dv), sk_of(tt + 1), sq);   \
     wait_vmem_prev_step<2 * C::CHUNKS_PER_WAVE>();                                                   \
     workgroup_barrier();                                                                             \
     issue_tile<D, false>(kh8, lim, tt + 4, KS + (KD) * C::TILE, dma);                                \
     issue_tile<D, true>(vh8, lim, tt + 2, VS + (VD) * C::TILE, dma);                                 \
-    fp8_phase2<D, CAUSAL, false>(S2, smem + VS + (VC) * C::TILE, smem + KS + (KR) * C::TILE, kops, lo, st, \
-                                 tt, N, lane, iw, my_q, c_of(tt + 1), true);                          \
+    fp8_phase2<D, CAUSAL, false, MX>(S2, smem + VS + (VC) * C::TILE, smem + KS + (KR) * C::TILE, kops, lo, \
+                                     st, tt, N, lane, iw, my_q, c_of(tt + 1), true, sv_of(tt));       \
   }
   for (;; t += 6) {
     FP8_MAIN(0, 2, 1, 0, 2, sa, sb)
@@ -491,16 +516,16 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
     const bool active = t <= kt_w;
     if (active) {
       const float dv = vd[t / TPB];
-      fp8_phase1<D, EXPM>(sa, sb, kops, qop, st, c_of(t), dvm * __builtin_amdgcn_rcpf(dv),
-                    __builtin_amdgcn_logf(dv) - log2_dvm);
+      fp8_phase1<D, EXPM, MX>(sa, sb, kops, qop, st, c_of(t), ir_of(dv), lr_of(dv), sk_of(t + 1), sq);
     }
     wait_vmem_all();
     workgroup_barrier();
     issue_tile<D, false>(kh8, lim, t + 4, KS + ((t + 1) % kRing) * C::TILE, dma);
     issue_tile<D, true>(vh8, lim, t + 2, VS + ((t + 2) % kRing) * C::TILE, dma);
     if (active) {
-      fp8_phase2<D, CAUSAL, true>(sb, smem + VS + (t % kRing) * C::TILE, smem + KS + ((t + 2) % kRing) * C::TILE,
-                                  kops, lo, st, t, N, lane, iw, my_q, c_of(t + 1), t + 1 <= kt_w);
+      fp8_phase2<D, CAUSAL, true, MX>(sb, smem + VS + (t % kRing) * C::TILE,
+                                      smem + KS + ((t + 2) % kRing) * C::TILE, kops, lo, st, t, N, lane, iw, my_q,
+                                      c_of(t + 1), t + 1 <= kt_w, sv_of(t));
 #pragma unroll
       for (int sub = 0; sub < C::NSUB; ++sub) sa[sub] = sb[sub];
     }
@@ -525,8 +550,10 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   }
 }
 
-#define FP8_INST(D, SB, CA, E) template __global__ void attn_fp8_kernel<D, SB, CA, E>(AttnFp8Params);
-#define FP8_INST_E(D, SB, CA) FP8_INST(D, SB, CA, kExpExact) FP8_INST(D, SB, CA, kExpSchraudolph)
+#define FP8_INST(D, SB, CA, E, MX) template __global__ void attn_fp8_kernel<D, SB, CA, E, MX>(AttnFp8Params);
+#define FP8_INST_E(D, SB, CA)                                                                 \
+  FP8_INST(D, SB, CA, kExpExact, false) FP8_INST(D, SB, CA, kExpSchraudolph, false)           \
+  FP8_INST(D, SB, CA, kExpExact, true) FP8_INST(D, SB, CA, kExpSchraudolph, true)
 FP8_INST_E(64, 64, false)
 FP8_INST_E(64, 64, true)
 FP8_INST_E(64, 128, false)
@@ -536,25 +563,30 @@ FP8_INST_E(128, 64, true)
 FP8_INST_E(128, 128, false)
 FP8_INST_E(128, 128, true)
 
-template <int D, int SB, int E>
-static void launch_dce(const AttnFp8Params& p, int causal, dim3 grid, hipStream_t stream) {
-  if (causal) attn_fp8_kernel<D, SB, true, E><<<grid, 256, 0, stream>>>(p);
-  else attn_fp8_kernel<D, SB, false, E><<<grid, 256, 0, stream>>>(p);
+template <int D, int SB, int E, bool MX>
+static void launch_dcem(const AttnFp8Params& p, int causal, dim3 grid, hipStream_t stream) {
+  if (causal) attn_fp8_kernel<D, SB, true, E, MX><<<grid, 256, 0, stream>>>(p);
+  else attn_fp8_kernel<D, SB, false, E, MX><<<grid, 256, 0, stream>>>(p);
 }
 
 template <int D, int SB>
-static void launch_dc(const AttnFp8Params& p, int causal, int exp_mode, dim3 grid, hipStream_t stream) {
-  if (exp_mode == kExpSchraudolph) launch_dce<D, SB, kExpSchraudolph>(p, causal, grid, stream);
-  else launch_dce<D, SB, kExpExact>(p, causal, grid, stream);
+static void launch_dc(const AttnFp8Params& p, int causal, int exp_mode, int mx, dim3 grid, hipStream_t stream) {
+  if (exp_mode == kExpSchraudolph) {
+    if (mx) launch_dcem<D, SB, kExpSchraudolph, true>(p, causal, grid, stream);
+    else launch_dcem<D, SB, kExpSchraudolph, false>(p, causal, grid, stream);
+  } else {
+    if (mx) launch_dcem<D, SB, kExpExact, true>(p, causal, grid, stream);
+    else launch_dcem<D, SB, kExpExact, false>(p, causal, grid, stream);
+  }
 }
 
-hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int BH,
+hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int mx, int BH,
                            hipStream_t stream) {
   dim3 grid(BH * p.n_qtiles);
-  if (D == 64 && SB == 64) launch_dc<64, 64>(p, causal, exp_mode, grid, stream);
-  else if (D == 64 && SB == 128) launch_dc<64, 128>(p, causal, exp_mode, grid, stream);
-  else if (D == 128 && SB == 64) launch_dc<128, 64>(p, causal, exp_mode, grid, stream);
-  else launch_dc<128, 128>(p, causal, exp_mode, grid, stream);
+  if (D == 64 && SB == 64) launch_dc<64, 64>(p, causal, exp_mode, mx, grid, stream);
+  else if (D == 64 && SB == 128) launch_dc<64, 128>(p, causal, exp_mode, mx, grid, stream);
+  else if (D == 128 && SB == 64) launch_dc<128, 64>(p, causal, exp_mode, mx, grid, stream);
+  else launch_dc<128, 128>(p, causal, exp_mode, mx, grid, stream);
   return hipGetLastError();
 }
 

@@ -54,9 +54,11 @@ constexpr int kQueriesPerWave = 32;
 constexpr int kQueryTile = kWaves * kQueriesPerWave;
 constexpr int kFp8KeyTile = 64;      // keys per tile in the FP8 kernel
 
-hipError_t launch_quantize(const QuantParams& p, int D, int SB, int BH, hipStream_t stream);
+// pow2: power-of-two (E8M0) block scales instead of amax / 448
+hipError_t launch_quantize(const QuantParams& p, int D, int SB, int pow2, int BH, hipStream_t stream);
 // exp_mode: 0 exact exponentials, 1 Schraudolph's bit-level approximation
-hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int BH,
+// mx: the block descales are powers of two and the matrix cores apply them
+hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int mx, int BH,
                            hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnBf16Params& p, int D, int causal, int BH, hipStream_t stream);
 

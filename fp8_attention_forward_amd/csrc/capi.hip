@@ -85,9 +85,10 @@ int launched(hipError_t e, const char* what) {
 
 extern "C" {
 
-int quantize_qkv_fp8(const float* q, const float* k, const float* v, int B, int H, int N, int D, int scale_block,
-                     int hadamard, uint64_t seed, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* q_descale,
-                     float* k_descale, float* v_descale, void* stream) {
+int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v, int B, int H, int N, int D,
+                          int scale_block, int hadamard, uint64_t seed, unsigned flags, uint8_t* q8, uint8_t* k8,
+                          uint8_t* v8, float* q_descale, float* k_descale, float* v_descale, void* stream) {
+  if (flags & ~(unsigned)ATTN_FP8_MX) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
   CHECK(check_sizes(B, H, N, D));
   CHECK(check_sb(scale_block));
   CHECK(check_ptr(q, 16, "q"));
@@ -111,13 +112,22 @@ int quantize_qkv_fp8(const float* q, const float* k, const float* v, int B, int 
   p.hadamard = hadamard ? 1 : 0;
   p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
   p.key1 = (uint32_t)(seed >> 32);
-  return launched(attnfp8::launch_quantize(p, D, scale_block, B * H, (hipStream_t)stream), "quantize_qkv_fp8");
+  return launched(attnfp8::launch_quantize(p, D, scale_block, (flags & ATTN_FP8_MX) ? 1 : 0, B * H,
+                                           (hipStream_t)stream),
+                  "quantize_qkv_fp8");
+}
+
+int quantize_qkv_fp8(const float* q, const float* k, const float* v, int B, int H, int N, int D, int scale_block,
+                     int hadamard, uint64_t seed, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* q_descale,
+                     float* k_descale, float* v_descale, void* stream) {
+  return quantize_qkv_fp8_opts(q, k, v, B, H, N, D, scale_block, hadamard, seed, 0u, q8, k8, v8, q_descale,
+                               k_descale, v_descale, stream);
 }
 
 int attn_fp8_fwd_opts(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_descale,
                       const float* k_descale, const float* v_descale, int B, int H, int N, int D, int scale_block,
                       int hadamard, int causal, unsigned flags, uint16_t* o_bf16, float* lse, void* stream) {
-  if (flags & ~(unsigned)ATTN_FP8_EXP2_SCHRAUDOLPH) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(unsigned)(ATTN_FP8_EXP2_SCHRAUDOLPH | ATTN_FP8_MX)) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
   CHECK(check_sizes(B, H, N, D));
   CHECK(check_sb(scale_block));
   CHECK(check_ptr(q8, 16, "q8"));
@@ -140,7 +150,9 @@ int attn_fp8_fwd_opts(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, c
   if (hadamard) sc /= D;
   p.score_scale = (float)sc;
   const int exp_mode = (flags & ATTN_FP8_EXP2_SCHRAUDOLPH) ? 1 : 0;
-  return launched(attnfp8::launch_attn_fp8(p, D, scale_block, causal ? 1 : 0, exp_mode, B * H, (hipStream_t)stream),
+  const int mx = (flags & ATTN_FP8_MX) ? 1 : 0;
+  return launched(attnfp8::launch_attn_fp8(p, D, scale_block, causal ? 1 : 0, exp_mode, mx, B * H,
+                                           (hipStream_t)stream),
                   "attn_fp8_fwd");
 }
 

@@ -16,6 +16,8 @@
 // amax over the block (wave + LDS reduction), inv = 448/a and descale = a/448
 // (correctly rounded), and code = e4m3(clamp(y * inv, +-448)) with the
 // hardware round-to-nearest-even convert; one 4-byte store per lane per row.
+// With power-of-two scales (the microscaling form, FLAMIA 2 Background) the
+// descale is the smallest 2^e that keeps the block's amax inside +-448.
 //
 // Memory: reads 4 B and writes 1 B per element (HBM bound).
 #include "common.h"
@@ -51,7 +53,25 @@ __device__ __forceinline__ void butterfly_xlane(float (&x)[4], int lane) {
   }
 }
 
-template <int D, int SB>
+// Power-of-two block scale (the MX form, E8M0): the smallest 2^e with
+// a <= 448 * 2^e, e clamped to [-127, 127], so no code of the block saturates;
+// a = 0 -> 2^0.  From the bits of a: a in [2^x, 2^(x+1)) with significand m;
+// 448 * 2^(x-8) = 1.75 * 2^x, so e = x - 8, plus one when m > 1.75.
+__device__ __forceinline__ int pow2_scale_exponent(float a) {
+  if (a == 0.0f) return 0;
+  const uint32_t b = __builtin_bit_cast(uint32_t, a);
+  const int x = (int)(b >> 23) - 127;
+  if (x == -127) return -127;                      // subnormal a: below 448 * 2^-127
+  int e = x - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^e as a float32 (e in [-127, 127]; 2^-127 is subnormal)
+__device__ __forceinline__ float exp2i(int e) {
+  return e >= -126 ? __builtin_bit_cast(float, (uint32_t)(e + 127) << 23) : __builtin_bit_cast(float, 0x00400000u);
+}
+
+template <int D, int SB, bool POW2>
 __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
 #pragma clang fp contract(off)
   constexpr int LPR = D / 4;              // lanes per row
@@ -125,8 +145,15 @@ __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
   if (lane == 0) red[wave] = m;
   __syncthreads();
   const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = a == 0.0f ? 1.0f : 448.0f / a;
-  const float descale = a == 0.0f ? 1.0f : a / 448.0f;
+  float inv, descale;
+  if constexpr (POW2) {
+    const int e = pow2_scale_exponent(a);
+    inv = exp2i(-e);
+    descale = exp2i(e);
+  } else {
+    inv = a == 0.0f ? 1.0f : 448.0f / a;
+    descale = a == 0.0f ? 1.0f : a / 448.0f;
+  }
   if (tid == 0) dsc[(size_t)bh * p.nblk + blk] = descale;
 
 #pragma unroll
@@ -141,19 +168,26 @@ __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
   }
 }
 
-#define QUANT_INST(D, SB) template __global__ void quantize_qkv_kernel<D, SB>(QuantParams);
+#define QUANT_INST(D, SB) \
+  template __global__ void quantize_qkv_kernel<D, SB, false>(QuantParams); \
+  template __global__ void quantize_qkv_kernel<D, SB, true>(QuantParams);
 QUANT_INST(64, 64)
 QUANT_INST(64, 128)
 QUANT_INST(128, 64)
 QUANT_INST(128, 128)
 
-hipError_t launch_quantize(const QuantParams& p, int D, int SB, int BH, hipStream_t stream) {
+template <int D, int SB>
+static void launch_q(const QuantParams& p, bool pow2, dim3 grid, hipStream_t stream) {
+  if (pow2) quantize_qkv_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
+  else quantize_qkv_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
+}
+
+hipError_t launch_quantize(const QuantParams& p, int D, int SB, int pow2, int BH, hipStream_t stream) {
   dim3 grid(p.nblk * BH, 3);
-  dim3 block(256);
-  if (D == 64 && SB == 64) quantize_qkv_kernel<64, 64><<<grid, block, 0, stream>>>(p);
-  else if (D == 64 && SB == 128) quantize_qkv_kernel<64, 128><<<grid, block, 0, stream>>>(p);
-  else if (D == 128 && SB == 64) quantize_qkv_kernel<128, 64><<<grid, block, 0, stream>>>(p);
-  else quantize_qkv_kernel<128, 128><<<grid, block, 0, stream>>>(p);
+  if (D == 64 && SB == 64) launch_q<64, 64>(p, pow2, grid, stream);
+  else if (D == 64 && SB == 128) launch_q<64, 128>(p, pow2, grid, stream);
+  else if (D == 128 && SB == 64) launch_q<128, 64>(p, pow2, grid, stream);
+  else launch_q<128, 128>(p, pow2, grid, stream);
   return hipGetLastError();
 }
 

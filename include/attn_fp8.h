@@ -62,12 +62,40 @@ typedef enum {
  *                       sigma_c = -1 when bit c of the 128-bit output is set.
  *   q8, k8, v8    out : e4m3 codes [B][H][N][D], code = e4m3_rne(clamp(y * inv, +-448))
  *   q/k/v_descale out : float32 [B][H][ceil(N/scale_block)], descale = amax/448
- *                       (inv = 448/amax; 1 for an all-zero block).
+ *                       (inv = 448/amax; 1 for an all-zero block).  A nonzero
+ *                       block amax below 448 / FLT_MAX (about 1.3e-36) makes
+ *                       inv overflow and is outside the contract of this rule
+ *                       (the power-of-two rule of ATTN_FP8_MX covers it).
  */
 int quantize_qkv_fp8(const float* q, const float* k, const float* v,
                      int B, int H, int N, int D, int scale_block, int hadamard, uint64_t seed,
                      uint8_t* q8, uint8_t* k8, uint8_t* v8,
                      float* q_descale, float* k_descale, float* v_descale, void* stream);
+
+/* Option flags of the *_opts entry points. */
+#define ATTN_FP8_EXP2_SCHRAUDOLPH 1u  /* attn_fp8_fwd_opts only; see below */
+/* ATTN_FP8_MX -- microscaling form of the block scales ("FLAMIA", 2 Background:
+ * blocks of low-bit codes sharing one scale, which block-scaled matrix units
+ * apply during accumulation).
+ *   quantize_qkv_fp8_opts: each block's descale is the smallest power of two
+ *     2^e with amax <= 448 * 2^e (e clamped to [-127, 127]; 2^0 for an
+ *     all-zero block), i.e. an E8M0 scale; code = e4m3_rne(y * 2^-e), which
+ *     never saturates.  Output layout as for quantize_qkv_fp8 (float32 2^e).
+ *   attn_fp8_fwd_opts: the descales must be powers of two (as written by
+ *     quantize_qkv_fp8_opts with ATTN_FP8_MX); their exponents are handed to
+ *     the scaled FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), which applies
+ *     them to Q, K and V inside the matrix core; P enters with scale 2^0.
+ *     Descales that are not powers of two give wrong results (only their
+ *     exponent fields are read). */
+#define ATTN_FP8_MX 2u
+
+/* quantize_qkv_fp8_opts -- quantize_qkv_fp8 with option flags (quantize_qkv_fp8
+ * is this call with flags = 0).  flags: ATTN_FP8_MX or 0; any other bit ->
+ * ATTN_EINVAL. */
+int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v,
+                          int B, int H, int N, int D, int scale_block, int hadamard, uint64_t seed,
+                          unsigned flags, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                          float* q_descale, float* k_descale, float* v_descale, void* stream);
 
 /* attn_fp8_fwd -- FP8 fused attention forward ("Fused attention kernel",
  * Implementation sketch: running max and sum, exp(old max - new max) rescale,
@@ -90,7 +118,9 @@ int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
 
 /* attn_fp8_fwd_opts -- attn_fp8_fwd with option flags (attn_fp8_fwd is this
  * call with flags = 0).
- *   flags             : ATTN_FP8_EXP2_SCHRAUDOLPH -> the probabilities use
+ *   flags             : any combination of ATTN_FP8_MX (above) and
+ *                       ATTN_FP8_EXP2_SCHRAUDOLPH.
+ *                       ATTN_FP8_EXP2_SCHRAUDOLPH -> the probabilities use
  *                       Schraudolph's bit-level exponential (N. N. Schraudolph,
  *                       "A fast, compact approximation of the exponential
  *                       function", Neural Computation 11(4), 1999) in base 2:
@@ -102,7 +132,6 @@ int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  *                       values; the O rescale factor stays exact.
  *                       Any other bit -> ATTN_EINVAL.
  */
-#define ATTN_FP8_EXP2_SCHRAUDOLPH 1u
 int attn_fp8_fwd_opts(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                       const float* q_descale, const float* k_descale, const float* v_descale,
                       int B, int H, int N, int D, int scale_block, int hadamard, int causal,

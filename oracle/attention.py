@@ -152,7 +152,7 @@ def brute_force_attention(q, k, v, causal, scale):
 
 def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
                                  causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True, block_c=64,
-                                 exp2="exact"):
+                                 exp2="exact", mx=False):
     """E2: the running-softmax loop over key blocks with P re-quantised to e4m3.
 
     The pages fix the loop (Implementation sketch) and that the matrix products
@@ -184,6 +184,12 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     of the whole exponent t - m + log2 r_j, as the kernel's option does:
     P = e4m3(S(t - m + log2 r_j)) and l sums S(t - m + log2 r_j) / r_j.  The
     rescale 2^(m_old - m_new) stays exact.
+
+    ``mx=True`` (power-of-two descales applied to the operands by the matrix
+    units): V's block scale multiplies V itself, so P = e4m3(2^(t - m)) carries
+    no r_j (dv_ref = 1), and O = O_acc / l with O_acc = sum P (v * dv_j).  With
+    power-of-two scales this differs from the default only where e4m3 rounding
+    of 2^(t-m) r_j and of 2^(t-m) differ (subnormal P).
     """
     if exp2 not in ("exact", "schraudolph"):
         raise ValueError("exp2 must be 'exact' or 'schraudolph'")
@@ -206,7 +212,9 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
         qh, kh, vh = q[idx][row_idx], k[idx], v[idx]
         qdr = qd[idx][row_idx // scale_block]
         own_blk = row_idx // scale_block
-        if causal:
+        if mx:
+            dv_ref = np.ones(len(row_idx))
+        elif causal:
             dv_ref = np.array([vd[idx][:b + 1].max() for b in own_blk])
         else:
             dv_ref = np.full(len(row_idx), vd[idx].max())
@@ -226,7 +234,7 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
             alpha = np.where(upd, np.exp2(np.where(np.isfinite(m), m - m_new, -np.inf)), 1.0)
             m = m_new
             ok = np.isfinite(m)
-            r = vd[idx][sb] / dv_ref
+            r = np.ones(len(row_idx)) if mx else vd[idx][sb] / dv_ref
             if exp2 == "exact":
                 pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
                 pu[~ok] = 0.0
@@ -238,7 +246,7 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
             if quantize_p:
                 pq = e4m3.decode(e4m3.encode(pq))
             l = alpha * l + pu.sum(axis=1)
-            acc = alpha[:, None] * acc + pq @ vh[k0:k1]
+            acc = alpha[:, None] * acc + pq @ (vh[k0:k1] * (vd[idx][sb] if mx else 1.0))
         o_all[idx] = acc * dv_ref[:, None] / l[:, None]
         lse_all[idx] = math.log(2.0) * (m + np.log2(l))
     if bf16_output:

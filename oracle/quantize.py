@@ -23,6 +23,15 @@ Readings taken here:
     transform of ``oracle.hadamard`` (unnormalised, stage order fixed).
 Dequantised value: e4m3_value(code) * descale.
 
+Power-of-two (microscaling, E8M0) scales, the option ``pow2=True`` ([P3]
+FLAMIA, 2 Background: MX formats give each block of low-bit codes one shared
+scale, applied by block-scaled matrix units).  The pages do not fix how the
+exponent is chosen; the reading taken is the power-of-two form of the scale
+above that never saturates: descale = 2^e with e the smallest integer such
+that a <= 448 * 2^e, clamped to the E8M0 range [-127, 127]; inv = 2^-e; a block
+of zeros gets 2^0.  (The scale rule of the OCP MX specification,
+2^(floor(log2 a) - 8), would clip the block maximum by up to 12.5%.)
+
 Everything below is float32 numpy arithmetic, which rounds every operation to
 nearest even, so the result is the bit pattern the specification defines.
 """
@@ -46,10 +55,24 @@ def rotate(x, signs):
     return fwht_f32(y)
 
 
-def quantize_tensor(x, scale_block, signs=None):
+def pow2_exponent(a):
+    """Smallest integer e with a <= 448 * 2^e (a float32 >= 0), clamped to [-127, 127]; 0 for a = 0.
+
+    Evaluated exactly: 448 * 2^e is exact in float64 over this range.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    _, ex = np.frexp(np.where(a > 0, a / 448.0, 1.0))   # a/448 = m 2^ex, m in [0.5, 1): exact for float32 a
+    e = ex - 1                                           # 2^(ex-1) <= a/448 < 2^ex
+    e = np.where(a <= 448.0 * np.exp2(e), e, e + 1)      # only exact powers of two stay at ex - 1
+    e = np.where(a > 0, e, 0)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_tensor(x, scale_block, signs=None, pow2=False):
     """One tensor [..., N, d] -> (codes uint8 [..., N, d], descale float32 [..., nblk]).
 
     ``signs`` (float32 +-1 of length d) turns the rotation on; None leaves x unrotated.
+    ``pow2`` selects the power-of-two (E8M0) block scales.
     """
     y = np.asarray(x, dtype=np.float32)
     if signs is not None:
@@ -62,15 +85,20 @@ def quantize_tensor(x, scale_block, signs=None):
         rows = y[..., blk * scale_block:min(n, (blk + 1) * scale_block), :]
         amax[..., blk] = np.abs(rows).max(axis=(-2, -1))
     zero = amax == 0
-    with np.errstate(divide="ignore", invalid="ignore"):
-        inv = np.where(zero, np.float32(1.0), _F448 / amax).astype(np.float32)
-        descale = np.where(zero, np.float32(1.0), amax / _F448).astype(np.float32)
+    if pow2:
+        e = pow2_exponent(amax)
+        inv = np.exp2(-e).astype(np.float32)             # exact: 2^-127 .. 2^127 are float32 values
+        descale = np.exp2(e).astype(np.float32)
+    else:
+        with np.errstate(divide="ignore", invalid="ignore"):
+            inv = np.where(zero, np.float32(1.0), _F448 / amax).astype(np.float32)
+            descale = np.where(zero, np.float32(1.0), amax / _F448).astype(np.float32)
     inv_rows = np.repeat(inv, scale_block, axis=-1)[..., :n]
     v = y * inv_rows[..., None]                 # float32 product, round to nearest even
     return e4m3.encode(v), descale
 
 
-def quantize_qkv(q, k, v, scale_block, hadamard, seed):
+def quantize_qkv(q, k, v, scale_block, hadamard, seed, pow2=False):
     """The full pre-processing of one attention call.
 
     Returns (q8, k8, v8, q_descale, k_descale, v_descale).  Q and K share one
@@ -78,9 +106,9 @@ def quantize_qkv(q, k, v, scale_block, hadamard, seed):
     """
     d = np.shape(q)[-1]
     signs = sign_vector(seed, d) if hadamard else None
-    q8, qd = quantize_tensor(q, scale_block, signs)
-    k8, kd = quantize_tensor(k, scale_block, signs)
-    v8, vd = quantize_tensor(v, scale_block, None)
+    q8, qd = quantize_tensor(q, scale_block, signs, pow2)
+    k8, kd = quantize_tensor(k, scale_block, signs, pow2)
+    v8, vd = quantize_tensor(v, scale_block, None, pow2)
     return q8, k8, v8, qd, kd, vd
 
 

@@ -106,12 +106,24 @@ def test_attn_fp8_rejects(lib, kw, frag):
 
 def test_attn_fp8_opts_rejects_unknown_flags(lib):
     args = [P, P, P, P, P, P, 1, 1, 64, 128, 128, 1, 0]
-    assert lib.attn_fp8_fwd_opts(*args, 2, P, P, None) == fa.ATTN_EINVAL
+    assert lib.attn_fp8_fwd_opts(*args, 4, P, P, None) == fa.ATTN_EINVAL
     assert "unknown flags" in fa.last_error()
+    assert lib.attn_fp8_fwd_opts(*args, 3, NUL, P, None) == fa.ATTN_EINVAL   # both options known: next check
+    assert "o_bf16 is NULL" in fa.last_error()
     assert lib.attn_fp8_fwd_opts(*args, 1, NUL, P, None) == fa.ATTN_EINVAL   # valid flag, then validation
     assert "o_bf16 is NULL" in fa.last_error()
     m = re.search(r"#define ATTN_FP8_EXP2_SCHRAUDOLPH (\d+)u", open(HEADER).read())
     assert int(m.group(1)) == fa.ATTN_FP8_EXP2_SCHRAUDOLPH
+
+
+def test_quantize_opts_flags(lib):
+    a = [P, P, P, 1, 1, 64, 128, 128, 1, 1]
+    assert lib.quantize_qkv_fp8_opts(*a, 1, P, P, P, P, P, P, None) == fa.ATTN_EINVAL   # EXP2 is not a quantiser flag
+    assert "unknown flags" in fa.last_error()
+    assert lib.quantize_qkv_fp8_opts(*a, 2, P, P, NUL, P, P, P, None) == fa.ATTN_EINVAL
+    assert "v8 is NULL" in fa.last_error()
+    m = re.search(r"#define ATTN_FP8_MX (\d+)u", open(HEADER).read())
+    assert int(m.group(1)) == fa.ATTN_FP8_MX
 
 
 def test_rejects_heads_too_long_for_32_bit_offsets(lib):

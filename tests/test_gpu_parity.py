@@ -53,15 +53,36 @@ def test_quantize_bit_exact(case):
             assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), f"{nm}: descales differ"
 
 
-def test_quantize_zero_and_extreme_blocks():
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}".format(*c[:6]))
+def test_quantize_pow2_scales_bit_exact(case):
+    B, H, N, D, sb, had, seed, kind = case
+    q, k, v = workloads.generate(kind, B, H, N, D, 500 + N)
+    out = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=sb, hadamard=had, seed=seed, mx=True)
+    torch.cuda.synchronize()
+    ref = oq.quantize_qkv(q, k, v, sb, had, seed, pow2=True)
+    for g, r, nm in zip((host(t) for t in out), ref, ("q8", "k8", "v8", "qd", "kd", "vd")):
+        if r.dtype == np.uint8:
+            assert np.array_equal(g, r), f"{case} {nm}: {np.count_nonzero(g != r)} codes differ"
+        else:
+            assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), f"{case} {nm}"
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quantize_zero_and_extreme_blocks(pow2):
     B, H, N, D, sb = 1, 2, 256, 128, 128
     q, k, v = workloads.generate("iid", B, H, N, D, 5)
     v[0, 0, :128] = 0.0                      # an all-zero block: descale 1, zero codes
     v[0, 0, 128:200] = -0.0
     q[0, 1, 5, 7] = 3.0e4                    # a huge outlier
     k[0, 1, 130:, :] *= 1e-30                # tiny values: subnormal e4m3 codes
-    got = [host(t) for t in gpu_quantize(q, k, v, sb, True, 11)]
-    ref = oq.quantize_qkv(q, k, v, sb, True, 11)
+    if pow2:
+        # the scale exponent clamps at -127 (the amax / 448 rule would overflow
+        # inv = 448 / amax below amax ~ 1.3e-36, outside its contract)
+        v[0, 1, 128:, :] *= 1e-38
+    out = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=sb, hadamard=True, seed=11, mx=pow2)
+    torch.cuda.synchronize()
+    got = [host(t) for t in out]
+    ref = oq.quantize_qkv(q, k, v, sb, True, 11, pow2=pow2)
     for g, r in zip(got, ref):
         assert np.array_equal(g.view(np.uint8) if g.dtype == np.uint8 else g.view(np.uint32),
                               r.view(np.uint8) if r.dtype == np.uint8 else r.view(np.uint32))
@@ -132,6 +153,30 @@ def test_attn_fp8_schraudolph_matches_emulation(case):
     assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
     oe, _ = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal)
     print(f"{case}: schraudolph RMSE vs its E2 {r2:.3e} (max {m2:.3e}); vs exact-exp E2 {rms(o - oe):.3e}")
+
+
+# Power-of-two block scales applied by the scaled FP8 MFMA (ATTN_FP8_MX), alone
+# and with the Schraudolph exponential, against E2 with the same options.
+MX_CASES = [c + (e,) for c in EXP2_CASES for e in ("exact",)] + \
+    [c + ("schraudolph",) for c in EXP2_CASES[2:5]]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}-{}".format(*c[:7], c[8]))
+def test_attn_fp8_mx_matches_emulation(case):
+    B, H, N, D, sb, had, causal, kind, exp2 = case
+    q, k, v = workloads.generate(kind, B, H, N, D, 300 + N)
+    q8, k8, v8, qd, kd, vd = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=sb, hadamard=had,
+                                                 seed=0x5EED, mx=True)
+    o, lse = fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=sb, hadamard=had, causal=causal,
+                             exp2=exp2, mx=True)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED, pow2=True)
+    o2, l2 = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2=exp2, mx=True)
+    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " mx vs E2")
+    assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
+    orf, _ = oatt.reference_attention(q, k, v, causal)
+    print(f"{case}: mx RMSE vs its E2 {r2:.3e} (max {m2:.3e}); vs FP64 {rms(o - orf):.3e}")
 
 
 BF16_CASES = [

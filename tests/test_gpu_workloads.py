@@ -101,6 +101,32 @@ def test_workload_fp8_schraudolph_parity(name):
               f"{rms(og - orf):.3e}", flush=True)
 
 
+@pytest.mark.parametrize("name", ["outlier", "outlier_causal"])
+def test_workload_fp8_mx_parity(name):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.generate_workload(w)
+    q8, k8, v8, qd, kd, vd = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=w.scale_block,
+                                                 hadamard=w.hadamard, seed=w.sign_seed, mx=True)
+    o, lse = fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=w.scale_block, hadamard=w.hadamard,
+                             causal=w.causal, mx=True)
+    torch.cuda.synchronize()
+    for (b, h) in _heads(w):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oq.quantize_qkv(q[sl], k[sl], v[sl], w.scale_block, w.hadamard, w.sign_seed, pow2=True)
+        got = [host(t[sl]) for t in (q8, k8, v8, qd, kd, vd)]
+        for g, r, nm in zip(got, ref, ("q8", "k8", "v8", "qd", "kd", "vd")):
+            same = np.array_equal(g, r) if g.dtype == np.uint8 else np.array_equal(g.view(np.uint32), r.view(np.uint32))
+            assert same, f"{name} mx head {(b, h)}: {nm}"
+        rows = sample_rows(w.N, 24, seed=b * 1000 + h)
+        o2, l2 = oatt.emulated_fp8_attention_tiled(*ref, w.scale_block, w.hadamard, w.causal, rows=rows, mx=True)
+        og = host(o[sl])[..., rows, :]
+        lg = host(lse[sl])[..., rows]
+        r2, m2 = check_fp8_output(og, lg, o2, l2, tag=f"{name} mx head {(b, h)}")
+        orf, _ = oatt.reference_attention(q[sl], k[sl], v[sl], w.causal, rows=rows)
+        print(f"[{name} mx] head {(b, h)}: vs E2 rmse {r2:.3e} max {m2:.3e}; vs FP64 rmse {rms(og - orf):.3e}",
+              flush=True)
+
+
 @pytest.mark.parametrize("name", ["outlier", "outlier_causal", "ablation_tail"])
 def test_workload_bf16_parity(name):
     w = workloads.WORKLOADS[name]

@@ -36,7 +36,7 @@ def kernels():
     for p in parts[1:]:
         name = p.split(":", 1)[0]
         funcs[name] = p.split("\n.Lfunc_end", 1)[0].splitlines()
-    assert len(funcs) == 16, sorted(funcs)   # D x scale block x causal x exponential mode
+    assert len(funcs) == 32, sorted(funcs)   # D x scale block x causal x exponential mode x MX
     return funcs
 
 

@@ -235,3 +235,48 @@ def test_tiled_fp8_loop_block_size_only_moves_p_rounding():
         assert np.allclose(o, o1, rtol=1e-11, atol=1e-13) and np.allclose(l, l1, rtol=1e-12)
     with pytest.raises(ValueError):
         attention.emulated_fp8_attention_tiled(*qq, 128, True, True, block_c=48)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_mx_loop_without_p_rounding_equals_e1(causal):
+    # power-of-two scales applied to the operands: without P rounding the loop
+    # is E1 on the same (pow2-quantised) inputs
+    shape = (1, 2, 300, 64)
+    q, k, v = (_rand(shape, s, 3.0).astype(np.float32) for s in (40, 41, 42))
+    v[0, 1, 128:192] *= 0.01
+    qq = quantize.quantize_qkv(q, k, v, 64, True, 0x5EED, pow2=True)
+    o1, l1 = attention.emulated_fp8_attention(*qq, 64, True, causal)
+    o2, l2 = attention.emulated_fp8_attention_tiled(*qq, 64, True, causal, quantize_p=False, bf16_output=False,
+                                                     mx=True)
+    assert np.allclose(o2, o1, rtol=1e-11, atol=1e-13)
+    assert np.allclose(l2, l1, rtol=1e-12, atol=1e-13)
+
+
+def test_tiled_mx_loop_brute_force_tiny():
+    # two key blocks of 2 keys, d = 4, pow2 scales: P = e4m3(2^(t - m)) with no
+    # V fold, V's scale on V itself
+    from oracle import e4m3
+    rng = np.random.default_rng(43)
+    shape = (1, 1, 4, 4)
+    q, k, v = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
+    v[0, 0, 2:] *= 0.1
+    qq = quantize.quantize_qkv(q, k, v, 2, False, 0, pow2=True)
+    q8, k8, v8, qd, kd, vd = qq
+    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=0.0, bf16_output=False, block_c=2,
+                                                     mx=True)
+    dq, dk, dv = (e4m3.decode(x)[0, 0] for x in (q8, k8, v8))
+    c = math.log2(math.e) / 2.0
+    for i in range(4):
+        t = [sum(dq[i, x] * dk[j, x] for x in range(4)) * qd[0, 0, i // 2] * kd[0, 0, j // 2] * c for j in range(4)]
+        m0 = max(t[0], t[1])
+        m1 = max(m0, t[2], t[3])
+        num = [0.0] * 4
+        for j in range(4):
+            mj = m0 if j < 2 else m1
+            pj = float(e4m3.decode(e4m3.encode(2.0 ** (t[j] - mj))))
+            for x in range(4):
+                num[x] += 2.0 ** (mj - m1) * pj * dv[j, x] * vd[0, 0, j // 2]
+        l = sum(2.0 ** (tj - m1) for tj in t)
+        for x in range(4):
+            assert o[0, 0, i, x] == pytest.approx(num[x] / l, rel=1e-12, abs=1e-14)
+        assert lse[0, 0, i] == pytest.approx(math.log(2) * (m1 + math.log2(l)), rel=1e-12)

@@ -119,3 +119,51 @@ def test_codes_are_never_nan():
     codes, _ = quantize.quantize_tensor(x, 64, None)
     assert not np.any((codes & 0x7F) == 0x7F)
     assert np.all(np.isfinite(e4m3.decode(codes)))
+
+
+# ---- power-of-two (E8M0) block scales: the smallest 2^e with amax <= 448 * 2^e
+
+@pytest.mark.parametrize("a,e", [
+    (448.0, 0), (449.0, 1), (1.0, -8), (1.75, -8), (float(np.nextafter(np.float32(1.75), np.float32(2))), -7),
+    (0.0, 0), (2.0 ** -140, -127), (1e38, 118), (224.0, -1), (224.5, 0), (896.0, 1), (3.0e-3, -17),
+])
+def test_pow2_exponent_worked_examples(a, e):
+    # hand-derived: 448 * 2^e >= a > 448 * 2^(e-1); e.g. a = 3e-3: 448 * 2^-17 = 3.42e-3 >= 3e-3 > 1.71e-3
+    assert int(quantize.pow2_exponent(np.float32(a))) == e
+
+
+def test_pow2_exponent_is_the_minimal_integer_brute_force():
+    rng = np.random.default_rng(5)
+    a = (rng.standard_normal(2000) * 10.0 ** rng.uniform(-30, 30, 2000)).astype(np.float32)
+    a = np.abs(a)
+    for x, e in zip(a, quantize.pow2_exponent(a)):
+        ok = [k for k in range(-127, 128) if float(x) <= 448.0 * 2.0 ** k]
+        assert int(e) == max(min(ok), -127)
+
+
+def test_pow2_block_scales_never_saturate_and_use_the_top_half_of_the_range():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((2, 3, 300, 64)).astype(np.float32) * np.float32(37.5)
+    codes, ds = quantize.quantize_tensor(x, 64, None, pow2=True)
+    m, e = np.frexp(ds.astype(np.float64))
+    assert np.all(m == 0.5)                                    # powers of two
+    vals = e4m3.decode(codes)
+    for blk in range(ds.shape[-1]):
+        v = np.abs(vals[..., blk * 64:(blk + 1) * 64, :]).max(axis=(-2, -1))
+        assert np.all(v <= 448) and np.all(v >= 224)           # amax / 2^e in (224, 448]
+    # the codes are the e4m3 rounding of x * 2^-e (exact power-of-two scaling)
+    inv = np.repeat(1.0 / ds.astype(np.float64), 64, axis=-1)[..., :300]
+    ref = e4m3.encode((x.astype(np.float64) * inv[..., None]).astype(np.float32))
+    assert np.array_equal(codes, ref)
+
+
+def test_pow2_zero_block_and_scale_invariance():
+    x = np.zeros((1, 128, 64), dtype=np.float32)
+    codes, ds = quantize.quantize_tensor(x, 64, None, pow2=True)
+    assert np.all(codes == 0) and np.all(ds == 1.0)
+    # scaling the input by a power of two moves only the block scales
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal((1, 128, 64)).astype(np.float32)
+    c1, d1 = quantize.quantize_tensor(y, 64, None, pow2=True)
+    c2, d2 = quantize.quantize_tensor(y * np.float32(8.0), 64, None, pow2=True)
+    assert np.array_equal(c1, c2) and np.array_equal(d2, d1 * 8)
