@@ -253,6 +253,20 @@ struct Fp8State {
   v8i pop;         // P^T of the last tile in e4m3 (B operand of the P V product)
 };
 
+// The rows of one attention sequence as the loop sees them.
+struct Fp8SeqView {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* qd;     // block descales of this sequence (block 0 first)
+  const float* kd;
+  const float* vd;
+  uint16_t* o;
+  float* lse;
+  int N;               // tokens
+  float score_scale;
+};
+
 // Mask + max + lazy reference update of a freshly computed score tile.
 // MASK = false: the tile is known to be complete and visible to every query
 // of the workgroup, and no mask code is emitted.
@@ -355,8 +369,11 @@ __device__ __forceinline__ void fp8_phase2(STile<D>& s_next, const uint8_t* vcur
   if (!MASK_NEXT || next_valid) tile_stats<D, CAUSAL, MASK_NEXT>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
 }
 
+// One query tile (128 queries) of one sequence: the whole loop.  The view
+// holds the sequence's rows (a head of the dense layout, or one document of a
+// packed head), its block descales and its output rows.
 template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
-__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
+__device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   using C = Fp8Cfg<D>;
   constexpr int TPB = SB / kBC;   // key tiles per scale block
   // three-slot rings for K (slots 0..2) and V (slots 3..5): a tile arrives two
@@ -366,29 +383,23 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = p.N;
-
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / p.n_qtiles;
-  int qt = logical % p.n_qtiles;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;            // longest tiles first
+  const int N = seq.N;
   const int i0 = qt * kQueryTile;
   const int iw = i0 + wave * kQueriesPerWave;
   const int my_q = iw + (lane & 31);
   const int h = lane >> 5;
 
-  const size_t head = (size_t)bh * N * D;
-  const uint8_t* kh8 = p.k8 + head;
-  const uint8_t* vh8 = p.v8 + head;
+  const uint8_t* kh8 = seq.k8;
+  const uint8_t* vh8 = seq.v8;
   // block descales are read-only for the whole launch: scalar loads
-  const cfloat* kd = (const cfloat*)(p.kd + (size_t)bh * p.nblk);
-  const cfloat* vd = (const cfloat*)(p.vd + (size_t)bh * p.nblk);
+  const cfloat* kd = (const cfloat*)seq.kd;
+  const cfloat* vd = (const cfloat*)seq.vd;
 
   // queries of this lane as the B operand: Q[q][64ks + 32h .. +31]
   v8i qop[C::KSTEPS];
   {
     const int qrow = my_q < N ? my_q : N - 1;
-    const uint8_t* qp = p.q8 + head + (size_t)qrow * D;
+    const uint8_t* qp = seq.q8 + (size_t)qrow * D;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       v4i lo = *(const v4i*)(qp + 64 * ks + 32 * h);
@@ -396,12 +407,14 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
       qop[ks] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
-  const int qblk = (my_q < N ? my_q : N - 1) / SB;
+  // (a wave's 32 queries lie in one scale block: SB is a multiple of 64 and
+  // iw of 32, and the clamp to N - 1 stays in the last block)
+  const int qblk = __builtin_amdgcn_readfirstlane((my_q < N ? my_q : N - 1) / SB);
   // MX: the matrix cores apply the power-of-two block scales (E8M0 exponents
   // sq, sk, sv), so the score scale is the constant score_scale and V needs no
   // fold into P
-  const float c_q = MX ? p.score_scale : p.qd[(size_t)bh * p.nblk + qblk] * p.score_scale;
-  const int sq = MX ? e8m0_of(p.qd[(size_t)bh * p.nblk + qblk]) : 0;
+  const float c_q = MX ? seq.score_scale : seq.qd[qblk] * seq.score_scale;
+  const int sq = MX ? e8m0_of(seq.qd[qblk]) : 0;
 
   const int n_kt = (N + kBC - 1) / kBC;
   int n_kt_wg = n_kt;              // key tiles the workgroup steps through
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   float dvm = 1.0f;
   if constexpr (!MX) {
     dvm = 0.0f;
-    for (int b = lane; b <= kt_w / TPB; b += 64) dvm = fmaxf(dvm, p.vd[(size_t)bh * p.nblk + b]);
+    for (int b = lane; b <= kt_w / TPB; b += 64) dvm = fmaxf(dvm, seq.vd[b]);
     dvm = wave_max(dvm);
   }
   const float log2_dvm = __builtin_amdgcn_logf(dvm);
@@ -536,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   const float l_tot = st.l_acc + swap_halves(st.l_acc);
   const float inv_l = dvm / l_tot;
   if (my_q < N) {
-    uint16_t* orow = p.o + head + (size_t)my_q * D;
+    uint16_t* orow = seq.o + (size_t)my_q * D;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -546,8 +559,30 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
         uint32_t w1 = pack_bf16x2(st.o[dt][4 * a + 2] * inv_l, st.o[dt][4 * a + 3] * inv_l);
         *(v2i*)(orow + d) = (v2i){(int)w0, (int)w1};
       }
-    if (h == 0) p.lse[(size_t)bh * N + my_q] = kLn2 * (st.m_ref + __builtin_amdgcn_logf(l_tot));
+    if (h == 0) seq.lse[my_q] = kLn2 * (st.m_ref + __builtin_amdgcn_logf(l_tot));
   }
+}
+
+// Dense layout: one workgroup per (batch x head, query tile).
+template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
+__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = logical / p.n_qtiles;
+  int qt = logical % p.n_qtiles;
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;            // longest tiles first
+  const size_t head = (size_t)bh * p.N * D;
+  Fp8SeqView seq;
+  seq.q8 = p.q8 + head;
+  seq.k8 = p.k8 + head;
+  seq.v8 = p.v8 + head;
+  seq.qd = p.qd + (size_t)bh * p.nblk;
+  seq.kd = p.kd + (size_t)bh * p.nblk;
+  seq.vd = p.vd + (size_t)bh * p.nblk;
+  seq.o = p.o + head;
+  seq.lse = p.lse + (size_t)bh * p.N;
+  seq.N = p.N;
+  seq.score_scale = p.score_scale;
+  attn_fp8_seq<D, SB, CAUSAL, EXPM, MX>(seq, qt);
 }
 
 #define FP8_INST(D, SB, CA, E, MX) template __global__ void attn_fp8_kernel<D, SB, CA, E, MX>(AttnFp8Params);
