@@ -34,13 +34,16 @@ Modules
              [P2 Overview, Implementation sketch]
   fastexp    Schraudolph's bit-level base-2 exponential (Neural Computation
              11(4), 1999), the option of E2 [P3 4.4 Bit-Level Exponentials]
+  varlen     packed variable-length documents: document-local blocks, attention
+             inside each document, the work items and their longest-first
+             order [P3 Abstract, 4.1 Performance on Packed Documents, 4.3]
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` to something
 other than itself (closed forms, an independent library, brute force,
 invariants).  Unpinned parts are listed in the functions that have them.
 """
 
-from . import e4m3, philox, hadamard, quantize, attention, fastexp  # noqa: F401
+from . import e4m3, philox, hadamard, quantize, attention, fastexp, varlen  # noqa: F401
 from .attention import (  # noqa: F401
     attention_fp64,
     reference_attention,

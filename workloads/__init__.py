@@ -22,6 +22,7 @@ Draw order (fixed): Q, K, V base values; then per tensor the outlier mask and
 outlier values (``outlier``), or the per-head channel ids (``channel``).
 """
 
+import math
 from dataclasses import dataclass, asdict
 
 import numpy as np
@@ -90,3 +91,96 @@ def generate(kind, B, H, N, D, seed):
 
 def generate_workload(w: Workload):
     return generate(w.kind, w.B, w.H, w.N, w.D, w.data_seed)
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length documents ([P3] FLAMIA, 4.1 Performance on Packed
+# Documents: 16 query heads, d = 128, up to T = 131072 packed tokens; its
+# workloads include equal-length and skewed length mixes, 4.3 Ablation Study).
+# The pages do not list the document lengths, so three seeded mixes stand in:
+#   * ``equal:L``: T / L documents of L tokens;
+#   * ``skewed:LO:HI``: lengths drawn log-uniformly from [LO, HI] until T is
+#     filled (the last document takes what is left);
+#   * ``long:F``: one document of F * T tokens first, then lengths drawn
+#     log-uniformly from [64, 2048] for the rest.
+# Layout [H][T][D] (heads outermost, packed tokens in document order);
+# cu_seqlens = [0, l_0, l_0 + l_1, ..., T] as int32.
+
+
+@dataclass(frozen=True)
+class PackedWorkload:
+    name: str
+    H: int
+    T: int
+    D: int
+    causal: bool
+    scale_block: int
+    hadamard: bool
+    kind: str          # value distribution, as for Workload
+    data_seed: int
+    mix: str           # length mix, see above
+    len_seed: int = 0
+    sign_seed: int = SIGN_SEED
+
+    def as_dict(self):
+        return asdict(self)
+
+    def cu_seqlens(self):
+        return cu_seqlens(doc_lengths(self.mix, self.T, self.len_seed))
+
+    def flops(self):
+        """Algorithmic FLOPs: 4 d per visible (query, key) pair, summed over documents."""
+        lens = np.diff(self.cu_seqlens()).astype(np.int64)
+        pairs = lens * (lens + 1) // 2 if self.causal else lens * lens
+        return int(4 * self.D * self.H * pairs.sum())
+
+
+def doc_lengths(mix, T, seed):
+    """Document lengths (int64 array summing to T) of a length mix."""
+    kind, _, arg = mix.partition(":")
+    rng = np.random.default_rng(seed)
+    if kind == "equal":
+        L = int(arg)
+        lens = [L] * (T // L) + ([T % L] if T % L else [])
+    elif kind in ("skewed", "long"):
+        lens = []
+        if kind == "long":
+            first = int(float(arg) * T)
+            lens.append(first)
+            lo, hi = 64, 2048
+        else:
+            lo, hi = (int(x) for x in arg.split(":"))
+        left = T - sum(lens)
+        while left > 0:
+            n = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+            n = min(max(n, 1), left)
+            lens.append(n)
+            left -= n
+    else:
+        raise ValueError(f"unknown length mix {mix!r}")
+    return np.asarray(lens, dtype=np.int64)
+
+
+def cu_seqlens(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+PACKED_WORKLOADS = {
+    "packed_skewed_causal": PackedWorkload("packed_skewed_causal", 16, 131072, 128, True, 128, True, "iid", 5,
+                                           "skewed:256:32768", 1),
+    "packed_equal_causal": PackedWorkload("packed_equal_causal", 16, 131072, 128, True, 128, True, "iid", 5,
+                                          "equal:4096"),
+    "packed_long_causal": PackedWorkload("packed_long_causal", 16, 131072, 128, True, 128, True, "iid", 5,
+                                         "long:0.5", 2),
+    "packed_skewed": PackedWorkload("packed_skewed", 16, 131072, 128, False, 128, True, "iid", 5,
+                                    "skewed:256:32768", 1),
+}
+
+
+def generate_packed(kind, H, T, D, seed):
+    """(q, k, v) float32 arrays of shape [H, T, D] (the [1, H, T, D] draw of ``generate``)."""
+    return tuple(t[0] for t in generate(kind, 1, H, T, D, seed))
+
+
+def generate_packed_workload(w: PackedWorkload):
+    return generate_packed(w.kind, w.H, w.T, w.D, w.data_seed)
