@@ -9,7 +9,9 @@ pairs discounted), quantisation included.  The same run also reports the
 attention alone, the attention options (Schraudolph exponentials; power-of-two
 block scales applied by the scaled MFMA), the quantiser alone, the BF16 twin, the accuracy against the
 FP64 oracle on a bounded sample, the roofline of the attention kernel and the
-oracle's CPU throughput.  Prints ONE JSON line.
+oracle's CPU throughput, and the packed variable-length document workloads
+(quantiser + attention with document-local scales, longest-first against
+document order).  Prints ONE JSON line.
 """
 
 import argparse
@@ -38,6 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and accuracy sample")
+    ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length document workloads")
     ap.add_argument("--attn-only", action="store_true", help="time only attn_fp8_fwd launches (for profiling)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="with --attn-only: first run one plain device copy of this many MiB (counter calibration)")
@@ -260,10 +263,76 @@ def main():
                       "device": torch.cuda.get_device_name(0)},
     }
 
+    if not args.no_packed:
+        result["packed_docs"] = packed_leg(args, fa, workloads, torch, dev, stream)
     if not args.no_cpu:
         result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch, o_mx))
     print(json.dumps(result))
     return 0
+
+
+PACKED_NAMES = ("packed_skewed_causal", "packed_long_causal", "packed_equal_causal", "packed_skewed")
+
+
+def packed_leg(args, fa, workloads, torch, dev, stream):
+    """Packed variable-length documents (FLAMIA's packed workloads: 16 heads,
+    d = 128, T = 131072): one step = quantize_qkv_fp8_varlen +
+    attn_fp8_fwd_varlen (schedule kernel + attention), inputs resident in HBM.
+    Also the attention alone in longest-first and in natural (document) order.
+    Every workload here draws the same tensors; only the document lengths differ."""
+    import numpy as np
+    out = {}
+    w0 = workloads.PACKED_WORKLOADS[PACKED_NAMES[0]]
+    q, k, v = (torch.from_numpy(x).to(dev) for x in workloads.generate_packed_workload(w0))
+    o = torch.empty((w0.H, w0.T, w0.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w0.H, w0.T), dtype=torch.float32, device=dev)
+    steps = max(5, args.steps // 4)
+    for name in PACKED_NAMES:
+        w = workloads.PACKED_WORKLOADS[name]
+        assert (w.kind, w.H, w.T, w.D, w.data_seed) == (w0.kind, w0.H, w0.T, w0.D, w0.data_seed)
+        cu_np = w.cu_seqlens()
+        cu = torch.from_numpy(cu_np).to(dev)
+        nd = len(cu_np) - 1
+        ws = torch.empty(fa.attn_fp8_varlen_workspace_bytes(w.T, nd), dtype=torch.uint8, device=dev)
+        qq = fa.quantize_qkv_fp8_varlen(q, k, v, cu, scale_block=w.scale_block, hadamard=w.hadamard,
+                                        seed=w.sign_seed)
+
+        def quant():
+            fa.quantize_qkv_fp8_varlen(q, k, v, cu, scale_block=w.scale_block, hadamard=w.hadamard,
+                                       seed=w.sign_seed, out=qq)
+
+        def attn(order="longest_first"):
+            fa.attn_fp8_fwd_varlen(*qq, cu, scale_block=w.scale_block, hadamard=w.hadamard, causal=w.causal,
+                                   out=(o, lse), order=order, workspace=ws)
+
+        def timed(fn, n):
+            for _ in range(2):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+
+        step_ms = timed(lambda: (quant(), attn()), steps)
+        attn_ms = timed(attn, steps)
+        nat_ms = timed(lambda: attn("natural"), steps)
+        quant_ms = timed(quant, steps)
+        flops = w.flops()
+        lens = np.diff(cu_np)
+        out[name] = {
+            "workload": f"H{w.H} T{w.T} D{w.D} {'causal' if w.causal else 'non-causal'}, {nd} documents "
+                        f"({w.mix}, lengths {int(lens.min())}..{int(lens.max())}), scale block {w.scale_block}, "
+                        f"{w.kind} inputs",
+            "tflops_step": round(flops / (step_ms * 1e-3) / 1e12, 2), "ms_step": round(step_ms, 4),
+            "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2), "attn_ms": round(attn_ms, 4),
+            "attn_natural_order_ms": round(nat_ms, 4),
+            "longest_first_speedup": round(nat_ms / attn_ms, 3),
+            "quantiser_ms": round(quant_ms, 4),
+        }
+    return out
 
 
 def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu):

@@ -10,6 +10,11 @@ is raised.
     o, lse = attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=128, hadamard=True, causal=False)
     o, lse = attn_fp8_fwd(..., exp2="schraudolph")   # Schraudolph's bit-level exponential
     o16, lse16 = attn_bf16_fwd(qb, kb, vb, causal=False)
+
+Packed variable-length documents ([H, T, D] tensors, int32 cu_seqlens on the device):
+
+    q8, k8, v8, qd, kd, vd = quantize_qkv_fp8_varlen(q, k, v, cu_seqlens, scale_block=128)
+    o, lse = attn_fp8_fwd_varlen(q8, k8, v8, qd, kd, vd, cu_seqlens, scale_block=128, causal=True)
 """
 
 import ctypes
@@ -20,15 +25,19 @@ import torch
 __all__ = [
     "LIB_PATH", "AttnError", "load_library", "quantize_qkv_fp8", "attn_fp8_fwd", "attn_bf16_fwd",
     "last_error", "abi_version", "EXPORTED_SYMBOLS", "ATTN_OK", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EHIP",
-    "ATTN_FP8_EXP2_SCHRAUDOLPH", "ATTN_FP8_MX", "EXP2_MODES",
+    "ATTN_FP8_EXP2_SCHRAUDOLPH", "ATTN_FP8_MX", "ATTN_FP8_NATURAL_ORDER", "EXP2_MODES", "ORDERS",
+    "quantize_qkv_fp8_varlen", "attn_fp8_fwd_varlen", "attn_fp8_varlen_workspace_bytes", "varlen_num_slots",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_fp8.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_FP8_EXP2_SCHRAUDOLPH = 1
 ATTN_FP8_MX = 2
+ATTN_FP8_NATURAL_ORDER = 4
+ORDERS = {"longest_first": 0, "natural": ATTN_FP8_NATURAL_ORDER}
 EXP2_MODES = {"exact": 0, "schraudolph": ATTN_FP8_EXP2_SCHRAUDOLPH}
 EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "quantize_qkv_fp8_opts", "attn_fp8_fwd", "attn_fp8_fwd_opts", "attn_bf16_fwd",
+                    "quantize_qkv_fp8_varlen", "attn_fp8_varlen_workspace_bytes", "attn_fp8_fwd_varlen",
                     "attn_fp8_last_error", "attn_fp8_abi_version")
 
 _lib = None
@@ -62,6 +71,14 @@ def load_library(path=None):
     lib.attn_fp8_fwd_opts.restype = i32
     lib.attn_bf16_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.attn_bf16_fwd.restype = i32
+    lib.quantize_qkv_fp8_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, u64, ctypes.c_uint,
+                                            vp, vp, vp, vp, vp, vp, vp]
+    lib.quantize_qkv_fp8_varlen.restype = i32
+    lib.attn_fp8_varlen_workspace_bytes.argtypes = [i32, i32]
+    lib.attn_fp8_varlen_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fp8_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_uint,
+                                        vp, ctypes.c_size_t, vp, vp, vp]
+    lib.attn_fp8_fwd_varlen.restype = i32
     lib.attn_fp8_last_error.argtypes = []
     lib.attn_fp8_last_error.restype = ctypes.c_char_p
     lib.attn_fp8_abi_version.argtypes = []
@@ -191,4 +208,97 @@ def attn_bf16_fwd(q, k, v, causal=False, out=None):
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
         B, H, N, D, int(bool(causal)), _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"),
         _stream(q)))
+    return out
+
+
+def _shape3(t, name):
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [H, T, D]")
+    return tuple(int(x) for x in t.shape)
+
+
+def _cu(cu_seqlens, T):
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D tensor of ndoc + 1 entries")
+    return _ptr(cu_seqlens, torch.int32, "cu_seqlens"), int(cu_seqlens.numel()) - 1
+
+
+def varlen_num_slots(T, ndoc, scale_block):
+    """Descale entries per head of packed documents: T // scale_block + ndoc."""
+    return T // scale_block + ndoc
+
+
+def attn_fp8_varlen_workspace_bytes(T, ndoc):
+    return int(load_library().attn_fp8_varlen_workspace_bytes(int(T), int(ndoc)))
+
+
+def quantize_qkv_fp8_varlen(q, k, v, cu_seqlens, scale_block=128, hadamard=True, seed=0x5EED, out=None, mx=False):
+    """Packed documents: q, k, v float32 [H, T, D], cu_seqlens int32 [ndoc + 1] (device).
+
+    Returns (q8, k8, v8 [H, T, D] uint8, q/k/v_descale [H, T // scale_block + ndoc] float32);
+    descale entries that belong to no block are left as allocated.
+    """
+    lib = load_library()
+    H, T, D = _shape3(q, "q")
+    if _shape3(k, "k") != (H, T, D) or _shape3(v, "v") != (H, T, D):
+        raise ValueError("q, k, v must have the same shape")
+    cu, ndoc = _cu(cu_seqlens, T)
+    ns = varlen_num_slots(T, ndoc, scale_block)
+    if out is None:
+        dev = q.device
+        out = tuple(torch.empty((H, T, D), dtype=torch.uint8, device=dev) for _ in range(3)) + \
+            tuple(torch.empty((H, ns), dtype=torch.float32, device=dev) for _ in range(3))
+    q8, k8, v8, qd, kd, vd = out
+    for t, nm in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if _shape3(t, nm) != (H, T, D):
+            raise ValueError(f"{nm} has the wrong shape")
+    for t, nm in ((qd, "q_descale"), (kd, "k_descale"), (vd, "v_descale")):
+        if tuple(t.shape) != (H, ns):
+            raise ValueError(f"{nm} must be [H, T // scale_block + ndoc]")
+    _check(lib.quantize_qkv_fp8_varlen(
+        _ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"), cu, ndoc,
+        H, T, D, int(scale_block), int(bool(hadamard)), int(seed) & 0xFFFFFFFFFFFFFFFF, ATTN_FP8_MX if mx else 0,
+        _ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
+        _ptr(qd, torch.float32, "q_descale"), _ptr(kd, torch.float32, "k_descale"),
+        _ptr(vd, torch.float32, "v_descale"), _stream(q)))
+    return out
+
+
+def attn_fp8_fwd_varlen(q8, k8, v8, q_descale, k_descale, v_descale, cu_seqlens, scale_block=128, hadamard=True,
+                        causal=False, out=None, exp2="exact", mx=False, order="longest_first", workspace=None):
+    """FP8 attention of packed documents; returns (o [H, T, D] bfloat16, lse [H, T] float32).
+
+    order: "longest_first" (default) or "natural" (ATTN_FP8_NATURAL_ORDER).
+    workspace: optional uint8 device tensor of at least
+    attn_fp8_varlen_workspace_bytes(T, ndoc) bytes (allocated here if None).
+    """
+    lib = load_library()
+    if exp2 not in EXP2_MODES:
+        raise ValueError(f"exp2 must be one of {sorted(EXP2_MODES)}")
+    if order not in ORDERS:
+        raise ValueError(f"order must be one of {sorted(ORDERS)}")
+    H, T, D = _shape3(q8, "q8")
+    if _shape3(k8, "k8") != (H, T, D) or _shape3(v8, "v8") != (H, T, D):
+        raise ValueError("q8, k8, v8 must have the same shape")
+    cu, ndoc = _cu(cu_seqlens, T)
+    ns = varlen_num_slots(T, ndoc, scale_block)
+    for t, nm in ((q_descale, "q_descale"), (k_descale, "k_descale"), (v_descale, "v_descale")):
+        if tuple(t.shape) != (H, ns):
+            raise ValueError(f"{nm} must be [H, T // scale_block + ndoc]")
+    need = attn_fp8_varlen_workspace_bytes(T, ndoc)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q8.device)
+    if out is None:
+        out = (torch.empty((H, T, D), dtype=torch.bfloat16, device=q8.device),
+               torch.empty((H, T), dtype=torch.float32, device=q8.device))
+    o, lse = out
+    if _shape3(o, "o") != (H, T, D) or tuple(lse.shape) != (H, T):
+        raise ValueError("o / lse have the wrong shape")
+    flags = EXP2_MODES[exp2] | (ATTN_FP8_MX if mx else 0) | ORDERS[order]
+    _check(lib.attn_fp8_fwd_varlen(
+        _ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
+        _ptr(q_descale, torch.float32, "q_descale"), _ptr(k_descale, torch.float32, "k_descale"),
+        _ptr(v_descale, torch.float32, "v_descale"), cu, ndoc, H, T, D, int(scale_block), int(bool(hadamard)),
+        int(bool(causal)), flags, _ptr(workspace, torch.uint8, "workspace"), ctypes.c_size_t(workspace.numel()),
+        _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _stream(q8)))
     return out

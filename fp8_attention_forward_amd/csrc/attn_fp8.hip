@@ -45,6 +45,8 @@
 //   * Causal: key tiles past the workgroup's last query are not loaded, tiles
 //     past a wave's last query are not computed, masks only on diagonal and
 //     tail tiles; query tiles are scheduled longest first.
+#include <type_traits>
+
 #include "common.h"
 #include "attn_internal.h"
 
@@ -585,7 +587,39 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
   attn_fp8_seq<D, SB, CAUSAL, EXPM, MX>(seq, qt);
 }
 
-#define FP8_INST(D, SB, CA, E, MX) template __global__ void attn_fp8_kernel<D, SB, CA, E, MX>(AttnFp8Params);
+// Packed documents ("FLAMIA", Abstract and 4.1 Performance on Packed
+// Documents: documents packed without repacking, document-local scales).
+// Workgroup w takes item w / H of the work list (document, query tile),
+// head w % H: heads of one item are neighbours, and the dispatcher's turn over
+// the 8 XCDs sends every item of a head to the same XCD when H is a multiple
+// of 8.  Workgroups past the item count leave before any barrier.
+template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
+__global__ __launch_bounds__(256, 2) void attn_fp8_varlen_kernel(AttnFp8VarlenParams p) {
+  const int e = blockIdx.x / p.H;
+  const int h = blockIdx.x - e * p.H;
+  if (e >= p.ws[0]) return;
+  const int2 item = ((const int2*)(p.ws + kWsHeaderInts))[e];
+  const int d = item.x;
+  const int a = p.cu[d];                  // checked by the schedule kernel: 0 <= a <= cu[d+1] <= T
+  const size_t row0 = (size_t)h * p.T + a;
+  const size_t slot0 = (size_t)h * p.nslot + a / SB + d;
+  Fp8SeqView seq;
+  seq.q8 = p.q8 + row0 * D;
+  seq.k8 = p.k8 + row0 * D;
+  seq.v8 = p.v8 + row0 * D;
+  seq.qd = p.qd + slot0;
+  seq.kd = p.kd + slot0;
+  seq.vd = p.vd + slot0;
+  seq.o = p.o + row0 * D;
+  seq.lse = p.lse + row0;
+  seq.N = p.cu[d + 1] - a;
+  seq.score_scale = p.score_scale;
+  attn_fp8_seq<D, SB, CAUSAL, EXPM, MX>(seq, item.y);
+}
+
+#define FP8_INST(D, SB, CA, E, MX)                                                  \
+  template __global__ void attn_fp8_kernel<D, SB, CA, E, MX>(AttnFp8Params);        \
+  template __global__ void attn_fp8_varlen_kernel<D, SB, CA, E, MX>(AttnFp8VarlenParams);
 #define FP8_INST_E(D, SB, CA)                                                                 \
   FP8_INST(D, SB, CA, kExpExact, false) FP8_INST(D, SB, CA, kExpSchraudolph, false)           \
   FP8_INST(D, SB, CA, kExpExact, true) FP8_INST(D, SB, CA, kExpSchraudolph, true)
@@ -598,14 +632,19 @@ FP8_INST_E(128, 64, true)
 FP8_INST_E(128, 128, false)
 FP8_INST_E(128, 128, true)
 
-template <int D, int SB, int E, bool MX>
-static void launch_dcem(const AttnFp8Params& p, int causal, dim3 grid, hipStream_t stream) {
-  if (causal) attn_fp8_kernel<D, SB, true, E, MX><<<grid, 256, 0, stream>>>(p);
-  else attn_fp8_kernel<D, SB, false, E, MX><<<grid, 256, 0, stream>>>(p);
+template <int D, int SB, int E, bool MX, class P>
+static void launch_dcem(const P& p, int causal, dim3 grid, hipStream_t stream) {
+  if constexpr (std::is_same<P, AttnFp8Params>::value) {
+    if (causal) attn_fp8_kernel<D, SB, true, E, MX><<<grid, 256, 0, stream>>>(p);
+    else attn_fp8_kernel<D, SB, false, E, MX><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (causal) attn_fp8_varlen_kernel<D, SB, true, E, MX><<<grid, 256, 0, stream>>>(p);
+    else attn_fp8_varlen_kernel<D, SB, false, E, MX><<<grid, 256, 0, stream>>>(p);
+  }
 }
 
-template <int D, int SB>
-static void launch_dc(const AttnFp8Params& p, int causal, int exp_mode, int mx, dim3 grid, hipStream_t stream) {
+template <int D, int SB, class P>
+static void launch_dc(const P& p, int causal, int exp_mode, int mx, dim3 grid, hipStream_t stream) {
   if (exp_mode == kExpSchraudolph) {
     if (mx) launch_dcem<D, SB, kExpSchraudolph, true>(p, causal, grid, stream);
     else launch_dcem<D, SB, kExpSchraudolph, false>(p, causal, grid, stream);
@@ -615,13 +654,25 @@ static void launch_dc(const AttnFp8Params& p, int causal, int exp_mode, int mx, 
   }
 }
 
-hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int mx, int BH,
-                           hipStream_t stream) {
-  dim3 grid(BH * p.n_qtiles);
+template <class P>
+static void launch_any(const P& p, int D, int SB, int causal, int exp_mode, int mx, dim3 grid, hipStream_t stream) {
   if (D == 64 && SB == 64) launch_dc<64, 64>(p, causal, exp_mode, mx, grid, stream);
   else if (D == 64 && SB == 128) launch_dc<64, 128>(p, causal, exp_mode, mx, grid, stream);
   else if (D == 128 && SB == 64) launch_dc<128, 64>(p, causal, exp_mode, mx, grid, stream);
   else launch_dc<128, 128>(p, causal, exp_mode, mx, grid, stream);
+}
+
+hipError_t launch_attn_fp8(const AttnFp8Params& p, int D, int SB, int causal, int exp_mode, int mx, int BH,
+                           hipStream_t stream) {
+  launch_any(p, D, SB, causal, exp_mode, mx, dim3(BH * p.n_qtiles), stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fp8_varlen(const VarlenSchedParams& sp, const AttnFp8VarlenParams& p, int D, int SB, int causal,
+                                  int exp_mode, int mx, int m_cap, hipStream_t stream) {
+  hipError_t e = launch_varlen_schedule(sp, stream);
+  if (e != hipSuccess) return e;
+  launch_any(p, D, SB, causal, exp_mode, mx, dim3(p.H * m_cap), stream);
   return hipGetLastError();
 }
 

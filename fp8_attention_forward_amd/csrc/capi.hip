@@ -58,6 +58,15 @@ int check_sizes(int B, int H, int N, int D) {
   return ATTN_OK;
 }
 
+int check_varlen_sizes(int H, int T, int ndoc, int D) {
+  if (H < 1 || T < 1 || ndoc < 1) return fail(ATTN_EINVAL, "H, T, ndoc must be >= 1 (got %d, %d, %d)", H, T, ndoc);
+  if (D != 64 && D != 128) return fail(ATTN_EINVAL, "D must be 64 or 128 (got %d)", D);
+  if (T > attnfp8::kVarlenMaxKeys * attnfp8::kQueryTile)
+    return fail(ATTN_EINVAL, "T must be <= %d (got %d)", attnfp8::kVarlenMaxKeys * attnfp8::kQueryTile, T);
+  if (ndoc > (1 << 24)) return fail(ATTN_EINVAL, "ndoc must be <= 2^24 (got %d)", ndoc);
+  return ATTN_OK;
+}
+
 int check_sb(int sb) {
   if (sb != 64 && sb != 128) return fail(ATTN_EINVAL, "scale_block must be 64 or 128 (got %d)", sb);
   return ATTN_OK;
@@ -179,6 +188,98 @@ int attn_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B
   p.n_qtiles = (N + attnfp8::kQueryTile - 1) / attnfp8::kQueryTile;
   p.score_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
   return launched(attnfp8::launch_attn_bf16(p, D, causal ? 1 : 0, B * H, (hipStream_t)stream), "attn_bf16_fwd");
+}
+
+size_t attn_fp8_varlen_workspace_bytes(int T, int ndoc) {
+  if (T < 1 || ndoc < 1) return 0;
+  const long long m_cap = ((long long)T + (long long)(attnfp8::kQueryTile - 1) * ndoc) / attnfp8::kQueryTile;
+  return (size_t)(4 * attnfp8::kWsHeaderInts) + 8 * (size_t)m_cap;
+}
+
+int quantize_qkv_fp8_varlen(const float* q, const float* k, const float* v, const int32_t* cu_seqlens, int ndoc,
+                            int H, int T, int D, int scale_block, int hadamard, uint64_t seed, unsigned flags,
+                            uint8_t* q8, uint8_t* k8, uint8_t* v8, float* q_descale, float* k_descale,
+                            float* v_descale, void* stream) {
+  if (flags & ~(unsigned)ATTN_FP8_MX) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
+  CHECK(check_varlen_sizes(H, T, ndoc, D));
+  CHECK(check_sb(scale_block));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(v, 16, "v"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(q8, 16, "q8"));
+  CHECK(check_ptr(k8, 16, "k8"));
+  CHECK(check_ptr(v8, 16, "v8"));
+  CHECK(check_ptr(q_descale, 4, "q_descale"));
+  CHECK(check_ptr(k_descale, 4, "k_descale"));
+  CHECK(check_ptr(v_descale, 4, "v_descale"));
+  const long long nslot = (long long)T / scale_block + ndoc;
+  if ((long long)H * nslot >= (1LL << 31)) return fail(ATTN_EINVAL, "H * (T / scale_block + ndoc) must be < 2^31");
+  CHECK(check_device());
+  attnfp8::QuantVarlenParams p;
+  p.q = q; p.k = k; p.v = v;
+  p.q8 = q8; p.k8 = k8; p.v8 = v8;
+  p.qd = q_descale; p.kd = k_descale; p.vd = v_descale;
+  p.cu = cu_seqlens;
+  p.ndoc = ndoc;
+  p.T = T;
+  p.nslot = (int)nslot;
+  p.hadamard = hadamard ? 1 : 0;
+  p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  p.key1 = (uint32_t)(seed >> 32);
+  return launched(attnfp8::launch_quantize_varlen(p, D, scale_block, (flags & ATTN_FP8_MX) ? 1 : 0, H,
+                                                  (hipStream_t)stream),
+                  "quantize_qkv_fp8_varlen");
+}
+
+int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_descale,
+                        const float* k_descale, const float* v_descale, const int32_t* cu_seqlens, int ndoc, int H,
+                        int T, int D, int scale_block, int hadamard, int causal, unsigned flags, void* workspace,
+                        size_t workspace_bytes, uint16_t* o_bf16, float* lse, void* stream) {
+  if (flags & ~(unsigned)(ATTN_FP8_EXP2_SCHRAUDOLPH | ATTN_FP8_MX | ATTN_FP8_NATURAL_ORDER))
+    return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
+  CHECK(check_varlen_sizes(H, T, ndoc, D));
+  CHECK(check_sb(scale_block));
+  CHECK(check_ptr(q8, 16, "q8"));
+  CHECK(check_ptr(k8, 16, "k8"));
+  CHECK(check_ptr(v8, 16, "v8"));
+  CHECK(check_ptr(q_descale, 4, "q_descale"));
+  CHECK(check_ptr(k_descale, 4, "k_descale"));
+  CHECK(check_ptr(v_descale, 4, "v_descale"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(workspace, 16, "workspace"));
+  CHECK(check_ptr(o_bf16, 16, "o_bf16"));
+  CHECK(check_ptr(lse, 4, "lse"));
+  const size_t need = attn_fp8_varlen_workspace_bytes(T, ndoc);
+  if (workspace_bytes < need)
+    return fail(ATTN_EINVAL, "workspace_bytes %zu < %zu (attn_fp8_varlen_workspace_bytes)", workspace_bytes, need);
+  const long long m_cap = ((long long)T + (long long)(attnfp8::kQueryTile - 1) * ndoc) / attnfp8::kQueryTile;
+  if ((long long)H * m_cap >= (1LL << 31)) return fail(ATTN_EINVAL, "H * (T + 127 ndoc) / 128 must be < 2^31");
+  CHECK(check_device());
+  attnfp8::VarlenSchedParams sp;
+  sp.cu = cu_seqlens;
+  sp.ndoc = ndoc;
+  sp.T = T;
+  sp.natural = (flags & ATTN_FP8_NATURAL_ORDER) ? 1 : 0;
+  sp.kmax = (T + attnfp8::kQueryTile - 1) / attnfp8::kQueryTile;
+  sp.ws = (int*)workspace;
+  attnfp8::AttnFp8VarlenParams p;
+  p.q8 = q8; p.k8 = k8; p.v8 = v8;
+  p.qd = q_descale; p.kd = k_descale; p.vd = v_descale;
+  p.o = o_bf16; p.lse = lse;
+  p.cu = cu_seqlens;
+  p.ws = (const int*)workspace;
+  p.T = T;
+  p.nslot = T / scale_block + ndoc;
+  p.H = H;
+  double sc = 1.4426950408889634 / std::sqrt((double)D);
+  if (hadamard) sc /= D;
+  p.score_scale = (float)sc;
+  const int exp_mode = (flags & ATTN_FP8_EXP2_SCHRAUDOLPH) ? 1 : 0;
+  const int mx = (flags & ATTN_FP8_MX) ? 1 : 0;
+  return launched(attnfp8::launch_attn_fp8_varlen(sp, p, D, scale_block, causal ? 1 : 0, exp_mode, mx, (int)m_cap,
+                                                  (hipStream_t)stream),
+                  "attn_fp8_fwd_varlen");
 }
 
 const char* attn_fp8_last_error(void) { return g_err; }

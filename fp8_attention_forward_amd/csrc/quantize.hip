@@ -71,36 +71,30 @@ __device__ __forceinline__ float exp2i(int e) {
   return e >= -126 ? __builtin_bit_cast(float, (uint32_t)(e + 127) << 23) : __builtin_bit_cast(float, 0x00400000u);
 }
 
+// One scale block: rows [0, nrows) (nrows <= SB) of src, D floats each ->
+// e4m3 codes at dst (same row layout) and the block's descale at *dsc.
+// Called by every thread of the workgroup (it holds a workgroup barrier).
 template <int D, int SB, bool POW2>
-__global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
+__device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, int nrows, float* dsc, bool rotate,
+                                               uint32_t key0, uint32_t key1) {
 #pragma clang fp contract(off)
   constexpr int LPR = D / 4;              // lanes per row
   constexpr int RPI = 256 / LPR;          // rows per iteration (whole workgroup)
   constexpr int ITERS = SB / RPI;
   static_assert(SB % RPI == 0, "block must be a whole number of iterations");
 
-  const int blk = blockIdx.x % p.nblk;
-  const int bh = blockIdx.x / p.nblk;
-  const int tensor = blockIdx.y;          // 0 = Q, 1 = K, 2 = V
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int rlane = tid % LPR;            // lane within its row group
   const int c0 = 4 * rlane;               // first channel held by this lane
-  const float* src = tensor == 0 ? p.q : (tensor == 1 ? p.k : p.v);
-  uint8_t* dst = tensor == 0 ? p.q8 : (tensor == 1 ? p.k8 : p.v8);
-  float* dsc = tensor == 0 ? p.qd : (tensor == 1 ? p.kd : p.vd);
-  const bool rotate = p.hadamard && tensor < 2;
-
-  const size_t head_off = (size_t)bh * p.N * D;
-  const int row0 = blk * SB;
 
   float x[ITERS][4];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    const int row = row0 + it * RPI + tid / LPR;
-    if (row < p.N) {
-      v4f t = *(const v4f*)(src + head_off + (size_t)row * D + c0);
+    const int row = it * RPI + tid / LPR;
+    if (row < nrows) {
+      v4f t = *(const v4f*)(src + (size_t)row * D + c0);
       x[it][0] = t[0]; x[it][1] = t[1]; x[it][2] = t[2]; x[it][3] = t[3];
     } else {
       x[it][0] = x[it][1] = x[it][2] = x[it][3] = 0.0f;
@@ -109,7 +103,7 @@ __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
 
   if (rotate) {
     uint32_t w[4];
-    philox_block(p.key0, p.key1, w);
+    philox_block(key0, key1, w);
     float sg[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -134,7 +128,7 @@ __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
     }
   }
 
-  // block amax (rows beyond N hold zeros and do not raise it)
+  // block amax (rows beyond the block hold zeros and do not raise it)
   float m = 0.0f;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it)
@@ -154,23 +148,92 @@ __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
     inv = a == 0.0f ? 1.0f : 448.0f / a;
     descale = a == 0.0f ? 1.0f : a / 448.0f;
   }
-  if (tid == 0) dsc[(size_t)bh * p.nblk + blk] = descale;
+  if (tid == 0) *dsc = descale;
 
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    const int row = row0 + it * RPI + tid / LPR;
+    const int row = it * RPI + tid / LPR;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(x[it][e] * inv, -448.0f), 448.0f);
     int packed = cvt_pk_fp8<false>(v[0], v[1], 0);
     packed = cvt_pk_fp8<true>(v[2], v[3], packed);
-    if (row < p.N) *(int*)(dst + head_off + (size_t)row * D + c0) = packed;
+    if (row < nrows) *(int*)(dst + (size_t)row * D + c0) = packed;
   }
+}
+
+// Dense layout: one workgroup per (block, batch*head) and tensor (blockIdx.y).
+template <int D, int SB, bool POW2>
+__global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
+  const int blk = blockIdx.x % p.nblk;
+  const int bh = blockIdx.x / p.nblk;
+  const int tensor = blockIdx.y;          // 0 = Q, 1 = K, 2 = V
+  const float* src = tensor == 0 ? p.q : (tensor == 1 ? p.k : p.v);
+  uint8_t* dst = tensor == 0 ? p.q8 : (tensor == 1 ? p.k8 : p.v8);
+  float* dsc = tensor == 0 ? p.qd : (tensor == 1 ? p.kd : p.vd);
+  const int row0 = blk * SB;
+  const size_t off = ((size_t)bh * p.N + row0) * D;
+  const int nrows = p.N - row0 < SB ? p.N - row0 : SB;
+  quantize_block<D, SB, POW2>(src + off, dst + off, nrows, dsc + (size_t)bh * p.nblk + blk,
+                              p.hadamard && tensor < 2, p.key0, p.key1);
+}
+
+// Packed documents ("FLAMIA", Abstract and 4.1 Performance on Packed
+// Documents: document-local scaling, no repacking).  Block b of document d
+// has descale slot first_slot(d) + b with first_slot(d) = cu[d] / SB + d,
+// strictly increasing in d, so a slot g belongs to the last document whose
+// first slot is <= g, or to none (the document has fewer blocks).  Entries of
+// cu are clamped to [0, T] so that any contents keep every access in bounds.
+template <int SB>
+__device__ __forceinline__ int doc_first_slot(const int* cu, int d, int T) {
+  int c = cu[d];
+  c = c < 0 ? 0 : (c > T ? T : c);
+  return c / SB + d;
+}
+
+// Largest d in [0, ndoc) with doc_first_slot(d) <= g (0 if none): a 64-way
+// search, one pivot per lane, the pivots that hold counted by a ballot.  Every
+// wave runs it on its own and gets the same answer.
+template <int SB>
+__device__ __forceinline__ int find_doc(const int* cu, int ndoc, int T, int g) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = ndoc;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool pred = idx < hi && doc_first_slot<SB>(cu, idx, T) <= g;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(pred));
+    lo += (cnt > 0 ? cnt - 1 : 0) * step;
+    hi = hi < lo + step ? hi : lo + step;
+  }
+  return lo;
+}
+
+template <int D, int SB, bool POW2>
+__global__ __launch_bounds__(256) void quantize_qkv_varlen_kernel(QuantVarlenParams p) {
+  const int g = blockIdx.x % p.nslot;
+  const int h = blockIdx.x / p.nslot;
+  const int tensor = blockIdx.y;
+  const int d = find_doc<SB>(p.cu, p.ndoc, p.T, g);
+  int a = p.cu[d], b = p.cu[d + 1];
+  a = a < 0 ? 0 : (a > p.T ? p.T : a);
+  b = b < a ? a : (b > p.T ? p.T : b);
+  const int r0 = a + (g - (a / SB + d)) * SB;
+  if (r0 < a || r0 >= b) return;          // a slot of no block (the same for the whole workgroup)
+  const float* src = tensor == 0 ? p.q : (tensor == 1 ? p.k : p.v);
+  uint8_t* dst = tensor == 0 ? p.q8 : (tensor == 1 ? p.k8 : p.v8);
+  float* dsc = tensor == 0 ? p.qd : (tensor == 1 ? p.kd : p.vd);
+  const size_t off = ((size_t)h * p.T + r0) * D;
+  const int nrows = b - r0 < SB ? b - r0 : SB;
+  quantize_block<D, SB, POW2>(src + off, dst + off, nrows, dsc + (size_t)h * p.nslot + g,
+                              p.hadamard && tensor < 2, p.key0, p.key1);
 }
 
 #define QUANT_INST(D, SB) \
   template __global__ void quantize_qkv_kernel<D, SB, false>(QuantParams); \
-  template __global__ void quantize_qkv_kernel<D, SB, true>(QuantParams);
+  template __global__ void quantize_qkv_kernel<D, SB, true>(QuantParams); \
+  template __global__ void quantize_qkv_varlen_kernel<D, SB, false>(QuantVarlenParams); \
+  template __global__ void quantize_qkv_varlen_kernel<D, SB, true>(QuantVarlenParams);
 QUANT_INST(64, 64)
 QUANT_INST(64, 128)
 QUANT_INST(128, 64)
@@ -180,6 +243,21 @@ template <int D, int SB>
 static void launch_q(const QuantParams& p, bool pow2, dim3 grid, hipStream_t stream) {
   if (pow2) quantize_qkv_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
   else quantize_qkv_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
+}
+
+template <int D, int SB>
+static void launch_qv(const QuantVarlenParams& p, bool pow2, dim3 grid, hipStream_t stream) {
+  if (pow2) quantize_qkv_varlen_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
+  else quantize_qkv_varlen_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
+}
+
+hipError_t launch_quantize_varlen(const QuantVarlenParams& p, int D, int SB, int pow2, int H, hipStream_t stream) {
+  dim3 grid(p.nslot * H, 3);
+  if (D == 64 && SB == 64) launch_qv<64, 64>(p, pow2, grid, stream);
+  else if (D == 64 && SB == 128) launch_qv<64, 128>(p, pow2, grid, stream);
+  else if (D == 128 && SB == 64) launch_qv<128, 64>(p, pow2, grid, stream);
+  else launch_qv<128, 128>(p, pow2, grid, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const QuantParams& p, int D, int SB, int pow2, int BH, hipStream_t stream) {

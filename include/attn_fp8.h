@@ -33,6 +33,7 @@
 #ifndef ATTN_FP8_H
 #define ATTN_FP8_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -147,6 +148,86 @@ int attn_bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int B, int H, int N, int D, int causal,
                   uint16_t* o_bf16, float* lse, void* stream);
 
+/* ---- Packed variable-length documents ----------------------------------
+ * "FLAMIA ..." (arXiv 2611.03344, Abstract and 4.1 Performance on Packed
+ * Documents): documents of different lengths are packed one after another
+ * with no padding and no repacking, every scale is local to one document, and
+ * attention runs inside each document.  4.3 Ablation Study: causal work runs
+ * longest first.  F. System Integration: scales and work lists stay on the
+ * GPU (no host synchronisation; graph capture works).
+ *
+ * Layout: Q, K, V, their codes and O are [H][T][D] (heads outermost, the T
+ * packed tokens of every head in document order); LSE is [H][T].
+ * cu_seqlens: DEVICE int32 [ndoc + 1], document d = tokens cu[d] .. cu[d+1]-1;
+ * it must start at 0, never decrease and end at T (empty documents are
+ * allowed).  The host never reads it.
+ * Scale blocks are document-local: the blocks of document d are its tokens in
+ * groups of scale_block from its first token (the last may be short).  The
+ * descale of block b of document d is entry cu[d] / scale_block + d + b of a
+ * head's row: descales are [H][T / scale_block + ndoc] (integer division);
+ * entries that belong to no block are not written.
+ * Sizes: H, T, ndoc >= 1; T <= 2^20; ndoc <= 2^24; D, scale_block as above;
+ * H * (T / scale_block + ndoc) < 2^31; H * ((T + 127 ndoc) / 128) < 2^31.
+ */
+
+/* Option flag of attn_fp8_fwd_varlen: schedule the work items in document
+ * order (documents ascending, query tiles ascending) instead of longest
+ * first.  It changes the order of the workgroups only, never a result: the
+ * baseline of FLAMIA's longest-first ablation. */
+#define ATTN_FP8_NATURAL_ORDER 4u
+
+/* quantize_qkv_fp8_varlen -- quantize_qkv_fp8_opts on packed documents.
+ *   q, k, v      in : float32 [H][T][D].
+ *   cu_seqlens   in : device int32 [ndoc + 1] (see above).
+ *   flags           : ATTN_FP8_MX or 0.
+ *   q8, k8, v8  out : e4m3 codes [H][T][D] (the rule of quantize_qkv_fp8 per block).
+ *   *_descale   out : float32 [H][T / scale_block + ndoc], slots as above.
+ * cu_seqlens contents that break the rule above give unspecified codes and
+ * descales; every access still stays inside the buffers (entries are clamped
+ * to [0, T]).
+ */
+int quantize_qkv_fp8_varlen(const float* q, const float* k, const float* v,
+                            const int32_t* cu_seqlens, int ndoc, int H, int T, int D,
+                            int scale_block, int hadamard, uint64_t seed, unsigned flags,
+                            uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                            float* q_descale, float* k_descale, float* v_descale, void* stream);
+
+/* attn_fp8_varlen_workspace_bytes -- bytes of device workspace that
+ * attn_fp8_fwd_varlen needs for T packed tokens in ndoc documents:
+ * 16 + 8 * ((T + 127 ndoc) / 128).  0 for T < 1 or ndoc < 1. */
+size_t attn_fp8_varlen_workspace_bytes(int T, int ndoc);
+
+/* attn_fp8_fwd_varlen -- attn_fp8_fwd_opts on packed documents.  Two
+ * launches on `stream`: one workgroup writes the work list (every (document,
+ * query tile of 128) item, longest first: documents in non-increasing tile
+ * count, each document's tiles together and from the last to the first, the
+ * last seeing the most keys under a causal mask) into the workspace; then
+ * the attention runs one workgroup per (item, head) in that order, the heads
+ * of one item next to each other.
+ *   q8 .. v_descale in : output of quantize_qkv_fp8_varlen with the same
+ *                        cu_seqlens, scale_block and hadamard flag.
+ *   causal             : nonzero -> query i of a document sees the keys of
+ *                        its document up to position i.
+ *   flags              : any combination of ATTN_FP8_EXP2_SCHRAUDOLPH,
+ *                        ATTN_FP8_MX and ATTN_FP8_NATURAL_ORDER.
+ *   workspace          : device memory, 16-byte aligned, at least
+ *                        attn_fp8_varlen_workspace_bytes(T, ndoc) bytes,
+ *                        owned by the caller; it holds the work list after
+ *                        the call: int32 item count, int32 status (0 = ok,
+ *                        1 = cu_seqlens broke the rule above), 8 unused bytes,
+ *                        then (document, query tile) int32 pairs in launch
+ *                        order.  Calls that share a workspace must not overlap.
+ *   o_bf16, lse    out : [H][T][D] bf16 bit patterns and [H][T] float32; rows
+ *                        of empty documents do not exist; with status 1 nothing
+ *                        is written.
+ */
+int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                        const float* q_descale, const float* k_descale, const float* v_descale,
+                        const int32_t* cu_seqlens, int ndoc, int H, int T, int D,
+                        int scale_block, int hadamard, int causal, unsigned flags,
+                        void* workspace, size_t workspace_bytes,
+                        uint16_t* o_bf16, float* lse, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none).
  * The string is owned by the library and valid until the next call on that thread. */
 const char* attn_fp8_last_error(void);
@@ -154,7 +235,7 @@ const char* attn_fp8_last_error(void);
 /* ABI version of this header (incremented on incompatible changes). */
 int attn_fp8_abi_version(void);
 
-#define ATTN_FP8_ABI_VERSION 2
+#define ATTN_FP8_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

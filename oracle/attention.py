@@ -150,9 +150,28 @@ def brute_force_attention(q, k, v, causal, scale):
     return np.array(o), np.array(lse)
 
 
+# Relative half-width of the window around an e4m3 rounding midpoint inside
+# which a probability evaluated in float32 (its exponent argument carries a
+# few float32 roundings of scores up to a few hundred in log2 units, and the
+# hardware exponential is within one ulp) can round to either neighbour.
+P_TIE_WINDOW = 2.0 ** -14
+
+
+def e4m3_tie_step(x, window=P_TIE_WINDOW):
+    """For x >= 0: the e4m3 spacing at x where x lies within ``window * x`` of
+    a rounding midpoint (so either neighbour is a valid rounding at a lower
+    precision), else 0."""
+    x = np.asarray(x, dtype=np.float64)
+    _, fexp = np.frexp(np.where(x > 0, x, 1.0))
+    quantum = np.ldexp(1.0, np.maximum(fexp - 1, -6) - 3)
+    frac = x / quantum - np.floor(x / quantum)
+    near = (x > 0) & (np.abs(frac - 0.5) * quantum <= window * x)
+    return np.where(near, quantum, 0.0)
+
+
 def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
                                  causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True, block_c=64,
-                                 exp2="exact", mx=False):
+                                 exp2="exact", mx=False, tie_slack=False):
     """E2: the running-softmax loop over key blocks with P re-quantised to e4m3.
 
     The pages fix the loop (Implementation sketch) and that the matrix products
@@ -190,6 +209,14 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     no r_j (dv_ref = 1), and O = O_acc / l with O_acc = sum P (v * dv_j).  With
     power-of-two scales this differs from the default only where e4m3 rounding
     of 2^(t-m) r_j and of 2^(t-m) differ (subnormal P).
+
+    ``tie_slack=True`` also returns, per output element, how far O can move
+    when every P whose unrounded value lies within ``P_TIE_WINDOW`` of an
+    e4m3 rounding midpoint (``e4m3_tie_step``) rounds to its other neighbour:
+    the sum of those rounding steps times |v| (dequantised), carried through
+    the rescales and the final normalisation like O itself.  It is the part of
+    a lower-precision evaluation's difference that is a valid rounding, not an
+    error.  Returns (O, LSE, slack) then.
     """
     if exp2 not in ("exact", "schraudolph"):
         raise ValueError("exp2 must be 'exact' or 'schraudolph'")
@@ -208,6 +235,7 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     nkb = -(-n // block_c)
     o_all = np.empty(lead + (len(row_idx), d))
     lse_all = np.empty(lead + (len(row_idx),))
+    slack_all = np.zeros(lead + (len(row_idx), d))
     for idx in np.ndindex(*lead):
         qh, kh, vh = q[idx][row_idx], k[idx], v[idx]
         qdr = qd[idx][row_idx // scale_block]
@@ -221,6 +249,7 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
         m = np.full(len(row_idx), -np.inf)
         l = np.zeros(len(row_idx))
         acc = np.zeros((len(row_idx), d))
+        slk = np.zeros((len(row_idx), d))
         for j in range(nkb):
             k0, k1 = j * block_c, min(n, (j + 1) * block_c)
             sb = k0 // scale_block
@@ -243,14 +272,21 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
                 pq = fastexp.schraudolph_exp2(t - np.where(ok, m, 0.0)[:, None] + np.log2(r)[:, None])
                 pq[~ok] = 0.0
                 pu = pq / r[:, None]
+            vblk = vh[k0:k1] * (vd[idx][sb] if mx else 1.0)
+            if tie_slack:
+                slk = alpha[:, None] * slk + (e4m3_tie_step(pq) if quantize_p else 0.0 * pq) @ np.abs(vblk)
             if quantize_p:
                 pq = e4m3.decode(e4m3.encode(pq))
             l = alpha * l + pu.sum(axis=1)
-            acc = alpha[:, None] * acc + pq @ (vh[k0:k1] * (vd[idx][sb] if mx else 1.0))
+            acc = alpha[:, None] * acc + pq @ vblk
         o_all[idx] = acc * dv_ref[:, None] / l[:, None]
         lse_all[idx] = math.log(2.0) * (m + np.log2(l))
+        if tie_slack:
+            slack_all[idx] = slk * dv_ref[:, None] / l[:, None]
     if bf16_output:
         o_all = round_to_bf16(o_all)
+    if tie_slack:
+        return o_all, lse_all, slack_all
     return o_all, lse_all
 
 

@@ -23,9 +23,12 @@ The pages leave the layout and the block rule open.  Readings taken here:
     the keys of its own document up to its own position;
   * work item = (document, query tile of 128 queries); its cost is the number
     of key tiles it visits: r + 1 for tile r of a causal document, the
-    document's tile count otherwise.  Longest-first = items in non-increasing
-    cost; the order among items of equal cost is free.  The natural order
-    (the ablation's baseline) is document-major, tiles ascending.
+    document's tile count otherwise.  Longest-first is read at the grain of
+    documents: documents in non-increasing tile count, each one's items
+    together, its tiles from the last (the costliest under a causal mask) to
+    the first; the order among documents of equal tile count is free.  The
+    natural order (the ablation's baseline) is document-major, tiles
+    ascending.
 """
 
 import math
@@ -114,41 +117,48 @@ def emulated_fp8_attention_varlen(q8, k8, v8, q_descale, k_descale, v_descale, c
 
     Each document is a sequence of its own: its codes, and the descales of its
     blocks read from its slots.  Keyword options (tau, quantize_p, bf16_output,
-    block_c, exp2, mx) pass through.  Returns (O [H, R, D], LSE [H, R]).
+    block_c, exp2, mx, tie_slack) pass through.  Returns (O [H, R, D], LSE
+    [H, R]) and, with tie_slack, the slack [H, R, D].
     """
     H, T, D = np.shape(q8)
     cu = check_cu(cu, T)
     rows, groups = _doc_rows(cu, rows, T)
     o = np.empty((H, len(rows), D))
     lse = np.empty((H, len(rows)))
+    slack = np.zeros((H, len(rows), D))
     for d, (loc, pos) in groups.items():
         a, b = int(cu[d]), int(cu[d + 1])
         s0 = first_slot(cu, d, scale_block)
         nb = -(-(b - a) // scale_block)
         sl = slice(s0, s0 + nb)
-        od, ld = emulated_fp8_attention_tiled(q8[:, a:b], k8[:, a:b], v8[:, a:b], q_descale[:, sl],
-                                              k_descale[:, sl], v_descale[:, sl], scale_block, hadamard, causal,
-                                              rows=loc, **kw)
-        o[:, pos] = od
-        lse[:, pos] = ld
+        res = emulated_fp8_attention_tiled(q8[:, a:b], k8[:, a:b], v8[:, a:b], q_descale[:, sl],
+                                           k_descale[:, sl], v_descale[:, sl], scale_block, hadamard, causal,
+                                           rows=loc, **kw)
+        o[:, pos] = res[0]
+        lse[:, pos] = res[1]
+        if kw.get("tie_slack"):
+            slack[:, pos] = res[2]
+    if kw.get("tie_slack"):
+        return o, lse, slack
     return o, lse
 
 
 def work_items(cu, causal, order="longest_first"):
     """The (document, query tile) items of one head and their costs, in ``order``.
 
-    Returns a list of (doc, tile, cost).  "longest_first": non-increasing cost,
-    ties by document then tile (any order of ties is valid); "natural":
-    document-major, tiles ascending.
+    Returns a list of (doc, tile, cost).  "longest_first": documents in
+    non-increasing tile count (ties by document index here; any order of
+    ties is valid), each document's tiles together and descending;
+    "natural": document-major, tiles ascending.
     """
     cu = np.asarray(cu, dtype=np.int64)
-    items = []
-    for d in range(len(cu) - 1):
-        nt = math.ceil(int(cu[d + 1] - cu[d]) / QUERY_TILE)
-        for r in range(nt):
-            items.append((d, r, r + 1 if causal else nt))
+    nts = [math.ceil(int(cu[d + 1] - cu[d]) / QUERY_TILE) for d in range(len(cu) - 1)]
     if order == "longest_first":
-        items.sort(key=lambda it: (-it[2], it[0], it[1]))
-    elif order != "natural":
+        docs = sorted(range(len(nts)), key=lambda d: (-nts[d], d))
+        tiles = lambda nt: range(nt - 1, -1, -1)
+    elif order == "natural":
+        docs = range(len(nts))
+        tiles = lambda nt: range(nt)
+    else:
         raise ValueError("order must be 'longest_first' or 'natural'")
-    return items
+    return [(d, r, r + 1 if causal else nts[d]) for d in docs for r in tiles(nts[d])]

@@ -46,13 +46,25 @@ def gpu_quantize(q, k, v, sb, hadamard, seed):
     return out
 
 
-def check_fp8_output(o_gpu, lse_gpu, o_ref, lse_ref, tag=""):
+def check_fp8_output(o_gpu, lse_gpu, o_ref, lse_ref, tag="", slack=None):
+    """RMSE and max-abs bounds on O, relative bound on LSE.
+
+    ``slack`` (the oracle's tie slack, same shape as O) widens the max-abs
+    bound element by element by what valid roundings of P at float32 precision
+    can move O: a P whose exact value sits on an e4m3 rounding midpoint may
+    round either way in the kernel."""
     err = o_gpu - o_ref
     rmse = float(np.sqrt(np.mean(err ** 2)))
     tol = FP8_MAX_TOL + ulp_bf16(o_ref)
+    strict = np.abs(err) > tol
+    if slack is not None:
+        tol = tol + slack
     worst = float(np.max(np.abs(err) - tol))
     assert rmse <= FP8_RMSE_TOL, f"{tag}: RMSE {rmse:.3e} > {FP8_RMSE_TOL}"
     assert worst <= 0, f"{tag}: max |err| exceeds bound by {worst:.3e} (max err {np.max(np.abs(err)):.3e})"
+    if slack is not None and strict.any():
+        print(f"{tag}: {int(strict.sum())} element(s) beyond {FP8_MAX_TOL} within the tie slack "
+              f"(max err {float(np.max(np.abs(err))):.3e})", flush=True)
     lerr = np.abs(lse_gpu - lse_ref)
     assert np.all(lerr <= LSE_REL_TOL * np.maximum(1.0, np.abs(lse_ref))), f"{tag}: LSE err {lerr.max():.3e}"
     return rmse, float(np.max(np.abs(err)))

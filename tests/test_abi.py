@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert fa.abi_version() == 2
+    assert fa.abi_version() == 3
     m = re.search(r"#define ATTN_FP8_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == fa.abi_version()
 
@@ -139,6 +139,80 @@ def test_rejects_heads_too_long_for_32_bit_offsets(lib):
 def test_attn_bf16_rejects(lib, kw, frag):
     assert _b(lib, **kw) == fa.ATTN_EINVAL
     assert frag in fa.last_error()
+
+
+def _qv(lib, **kw):
+    a = dict(q=P, k=P, v=P, cu=P, ndoc=3, H=2, T=1000, D=128, sb=128, had=1, seed=1, flags=0, q8=P, k8=P, v8=P,
+             qd=P, kd=P, vd=P)
+    a.update(kw)
+    return lib.quantize_qkv_fp8_varlen(a["q"], a["k"], a["v"], a["cu"], a["ndoc"], a["H"], a["T"], a["D"], a["sb"],
+                                       a["had"], a["seed"], a["flags"], a["q8"], a["k8"], a["v8"], a["qd"], a["kd"],
+                                       a["vd"], None)
+
+
+def _av(lib, **kw):
+    a = dict(q8=P, k8=P, v8=P, qd=P, kd=P, vd=P, cu=P, ndoc=3, H=2, T=1000, D=128, sb=128, had=1, causal=1, flags=0,
+             ws=P, wsb=1 << 20, o=P, lse=P)
+    a.update(kw)
+    return lib.attn_fp8_fwd_varlen(a["q8"], a["k8"], a["v8"], a["qd"], a["kd"], a["vd"], a["cu"], a["ndoc"], a["H"],
+                                   a["T"], a["D"], a["sb"], a["had"], a["causal"], a["flags"], a["ws"], a["wsb"],
+                                   a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(ndoc=0), ">= 1"),
+    (dict(T=0), ">= 1"),
+    (dict(T=(1 << 20) + 1), "T must be <= 1048576"),
+    (dict(D=96), "D must be 64 or 128"),
+    (dict(sb=256), "scale_block"),
+    (dict(cu=NUL), "cu_seqlens is NULL"),
+    (dict(cu=ctypes.c_void_p(0x10002)), "cu_seqlens is not 4-byte aligned"),
+    (dict(flags=1), "unknown flags"),
+    (dict(flags=4), "unknown flags"),
+    (dict(vd=NUL), "v_descale is NULL"),
+    (dict(H=1 << 17, T=1 << 20, sb=64), "2^31"),
+])
+def test_quantize_varlen_rejects(lib, kw, frag):
+    assert _qv(lib, **kw) == fa.ATTN_EINVAL
+    assert frag in fa.last_error()
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(ndoc=-1), ">= 1"),
+    (dict(ndoc=(1 << 24) + 1), "ndoc must be <= 2^24"),
+    (dict(D=32), "D must be 64 or 128"),
+    (dict(flags=8), "unknown flags"),
+    (dict(ws=NUL), "workspace is NULL"),
+    (dict(ws=MIS), "workspace is not 16-byte aligned"),
+    (dict(wsb=16 + 8 * ((1000 + 127 * 3) // 128) - 1), "workspace_bytes"),
+    (dict(o=MIS), "o_bf16 is not 16-byte aligned"),
+    (dict(cu=NUL), "cu_seqlens is NULL"),
+    (dict(H=1 << 20, T=1 << 20, ndoc=1000), "2^31"),
+])
+def test_attn_fp8_varlen_rejects(lib, kw, frag):
+    assert _av(lib, **kw) == fa.ATTN_EINVAL
+    assert frag in fa.last_error()
+
+
+def test_varlen_flags_and_workspace_size(lib):
+    # every known flag passes the flag check (the NULL output fails next)
+    assert _av(lib, flags=7, o=NUL) == fa.ATTN_EINVAL and "o_bf16 is NULL" in fa.last_error()
+    assert _qv(lib, flags=2, q8=NUL) == fa.ATTN_EINVAL and "q8 is NULL" in fa.last_error()
+    m = re.search(r"#define ATTN_FP8_NATURAL_ORDER (\d+)u", open(HEADER).read())
+    assert int(m.group(1)) == fa.ATTN_FP8_NATURAL_ORDER
+    # 16 header bytes + 8 per possible item; the items of T tokens in ndoc
+    # documents are at most sum ceil(l / 128) <= (T + 127 ndoc) / 128
+    assert fa.attn_fp8_varlen_workspace_bytes(1000, 3) == 16 + 8 * ((1000 + 381) // 128)
+    assert fa.attn_fp8_varlen_workspace_bytes(128, 1) == 16 + 8
+    assert fa.attn_fp8_varlen_workspace_bytes(0, 1) == 0 and fa.attn_fp8_varlen_workspace_bytes(5, 0) == 0
+    import itertools
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        T, nd = int(rng.integers(1, 5000)), int(rng.integers(1, 50))
+        cuts = np.sort(rng.integers(0, T + 1, nd - 1))
+        lens = np.diff(np.concatenate([[0], cuts, [T]]))
+        assert 16 + 8 * int(sum(-(-l // 128) for l in lens)) <= fa.attn_fp8_varlen_workspace_bytes(T, nd)
 
 
 def test_binding_refuses_host_tensors():

@@ -117,14 +117,14 @@ def test_attn_fp8_matches_emulated_fp8(case):
     o, lse = _fp8_run(q, k, v, sb, had, causal)
     qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED)
     # the same pipeline emulated (P re-quantised to e4m3 as the kernel does)
-    o2, l2 = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal)
+    o2, l2, slk = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, tie_slack=True)
     if kind == "channel" and not had:
         # unrotated channel outliers: FP8 MFMA group accumulation error in S
         # dominates (see LOOSE in test_gpu_workloads)
         r2, m2 = rms(o - o2), float(np.max(np.abs(o - o2)))
         assert r2 <= 2e-2 and np.all(np.abs(lse - l2) <= 2e-2 * np.maximum(1.0, np.abs(l2)))
     else:
-        r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " vs E2")
+        r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " vs E2", slack=slk)
         # what is left is the BF16 rounding of O, the FP8 accumulation of the
         # matrix cores and rare flips of a P rounding
         assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
@@ -148,8 +148,8 @@ def test_attn_fp8_schraudolph_matches_emulation(case):
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
     qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED)
-    o2, l2 = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2="schraudolph")
-    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " schraudolph vs E2")
+    o2, l2, slk = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2="schraudolph", tie_slack=True)
+    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " schraudolph vs E2", slack=slk)
     assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
     oe, _ = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal)
     print(f"{case}: schraudolph RMSE vs its E2 {r2:.3e} (max {m2:.3e}); vs exact-exp E2 {rms(o - oe):.3e}")
@@ -172,8 +172,8 @@ def test_attn_fp8_mx_matches_emulation(case):
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
     qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED, pow2=True)
-    o2, l2 = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2=exp2, mx=True)
-    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " mx vs E2")
+    o2, l2, slk = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2=exp2, mx=True, tie_slack=True)
+    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " mx vs E2", slack=slk)
     assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
     orf, _ = oatt.reference_attention(q, k, v, causal)
     print(f"{case}: mx RMSE vs its E2 {r2:.3e} (max {m2:.3e}); vs FP64 {rms(o - orf):.3e}")

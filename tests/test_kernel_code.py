@@ -31,12 +31,13 @@ def kernels():
            "-packed-fp32-ops", "--cuda-device-only", "-S", SRC, "-o", "-"]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stderr[-2000:]
-    parts = re.split(r"\n(?=_ZN7attnfp815attn_fp8_kernel\S*:)", res.stdout)
+    parts = re.split(r"\n(?=_ZN7attnfp8(?:15attn_fp8_kernel|22attn_fp8_varlen_kernel)\S*:)", res.stdout)
     funcs = {}
     for p in parts[1:]:
         name = p.split(":", 1)[0]
         funcs[name] = p.split("\n.Lfunc_end", 1)[0].splitlines()
-    assert len(funcs) == 32, sorted(funcs)   # D x scale block x causal x exponential mode x MX
+    # (dense, packed) x D x scale block x causal x exponential mode x MX
+    assert len(funcs) == 64, sorted(funcs)
     return funcs
 
 

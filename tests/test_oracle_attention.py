@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import scipy.linalg
 
-from oracle import attention, quantize
+from oracle import attention, e4m3, quantize
 from oracle.philox import sign_vector
 
 
@@ -280,3 +280,54 @@ def test_tiled_mx_loop_brute_force_tiny():
         for x in range(4):
             assert o[0, 0, i, x] == pytest.approx(num[x] / l, rel=1e-12, abs=1e-14)
         assert lse[0, 0, i] == pytest.approx(math.log(2) * (m1 + math.log2(l)), rel=1e-12)
+
+
+# ---- the tie slack of E2: how far valid lower-precision roundings of P can move O
+
+def test_e4m3_tie_step_at_every_midpoint():
+    vals = np.unique(np.abs(e4m3.decode(e4m3.all_finite_codes())))
+    vals = vals[vals > 0]
+    lo, hi = vals[:-1], vals[1:]
+    mid = (lo + hi) / 2
+    assert np.array_equal(attention.e4m3_tie_step(mid), hi - lo)
+    assert np.all(attention.e4m3_tie_step(vals) == 0)                 # representable: no tie
+    w = attention.P_TIE_WINDOW
+    assert np.array_equal(attention.e4m3_tie_step(mid * (1 + w / 2)), hi - lo)
+    assert np.all(attention.e4m3_tie_step(mid * (1 + 2 * w)) == 0)
+    assert np.all(attention.e4m3_tie_step(mid * (1 - 2 * w)) == 0)
+    assert attention.e4m3_tie_step(0.0) == 0
+
+
+def test_tie_slack_of_a_probability_on_a_midpoint():
+    # two keys with scores s0 = 2 and s1 = 1 for both queries, c = log2(32/31):
+    # P_0 = 1 exactly, P_1 = 2^-c = 31/32 = 0.96875, the midpoint of 0.9375 and
+    # 1.0 (it rounds to the even 1.0); the slack is 0.0625 |v_1| dv / l with
+    # l = 1 + 31/32
+    d = 64
+    q = np.zeros((1, 2, d)); q[0, :, 0] = 1.0
+    k = np.zeros((1, 2, d)); k[0, 0, 0] = 2.0; k[0, 1, 0] = 1.0
+    v = np.random.default_rng(0).standard_normal((1, 2, d)) * 8
+    q8, k8, v8 = e4m3.encode(q), e4m3.encode(k), e4m3.encode(v)
+    c = math.log2(32 / 31)
+    score_scale = math.log2(math.e) / math.sqrt(d)
+    qd, kd, vd = np.full((1, 1), c / score_scale), np.ones((1, 1)), np.full((1, 1), 0.25)
+    o, lse, slack = attention.emulated_fp8_attention_tiled(q8, k8, v8, qd, kd, vd, 64, False, False,
+                                                           bf16_output=False, tie_slack=True)
+    vv = e4m3.decode(v8[0])
+    l = 1 + 31 / 32
+    assert np.allclose(slack[0], np.abs(vv[1]) * 0.0625 * 0.25 / l, rtol=1e-12, atol=0)
+    assert np.allclose(o[0], (vv[0] + 1.0 * vv[1]) * 0.25 / l, rtol=1e-12)        # P_1 rounded to 1.0
+    _, _, s2 = attention.emulated_fp8_attention_tiled(q8, k8, v8, qd, kd, vd, 64, False, False,
+                                                      quantize_p=False, tie_slack=True)
+    assert np.all(s2 == 0)
+
+
+def test_tie_slack_is_small_and_leaves_o_unchanged():
+    n, d = 256, 64
+    rng = np.random.default_rng(3)
+    q8, k8, v8 = (e4m3.encode(rng.standard_normal((1, n, d)) * 30) for _ in range(3))
+    ds = [rng.uniform(0.005, 0.02, (1, 4)) for _ in range(3)]
+    o, l = attention.emulated_fp8_attention_tiled(q8, k8, v8, *ds, 64, True, True)
+    o2, l2, sl = attention.emulated_fp8_attention_tiled(q8, k8, v8, *ds, 64, True, True, tie_slack=True)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    assert np.all(sl >= 0) and np.mean(sl > 0) < 0.05

@@ -254,5 +254,14 @@ def test_work_items(causal):
                 brute.append((d, r, -(-keys // 128)))
                 r += 1
         assert sorted(lf) == sorted(brute) and nat == brute
-        costs = [c for _, _, c in lf]
-        assert all(x >= y for x, y in zip(costs, costs[1:]))
+        # longest first: documents by non-increasing tile count, each one's
+        # tiles together and descending (so the costliest causal tile first)
+        docs = [d for i, (d, _, _) in enumerate(lf) if i == 0 or lf[i - 1][0] != d]
+        assert len(docs) == len(set(docs))
+        nts = [sum(1 for it in brute if it[0] == d) for d in docs]
+        assert all(x >= y for x, y in zip(nts, nts[1:]))
+        for d in docs:
+            rs = [r for dd, r, _ in lf if dd == d]
+            assert rs == sorted(rs, reverse=True)
+        if causal and lf:
+            assert lf[0][2] == max(c for _, _, c in brute)

@@ -23,6 +23,8 @@ outlier values (``outlier``), or the per-head channel ids (``channel``).
 """
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, asdict
 
 import numpy as np
@@ -178,8 +180,30 @@ PACKED_WORKLOADS = {
 
 
 def generate_packed(kind, H, T, D, seed):
-    """(q, k, v) float32 arrays of shape [H, T, D] (the [1, H, T, D] draw of ``generate``)."""
-    return tuple(t[0] for t in generate(kind, 1, H, T, D, seed))
+    """(q, k, v) float32 arrays of shape [H, T, D].
+
+    Every (tensor, head) slice has its own PCG64 stream, child i = 3 * h + t
+    (t = 0, 1, 2 for Q, K, V) of SeedSequence(seed): its N(0, 1) base values,
+    then for ``outlier`` its 0.1% mask and N(0, 10^2) outlier values.  The
+    slices are independent, so they are drawn on several threads.
+    """
+    if kind not in ("iid", "outlier"):
+        raise ValueError(f"packed inputs support the iid and outlier kinds, not {kind!r}")
+    out = np.empty((3, H, T, D), dtype=np.float32)
+    children = np.random.SeedSequence(seed).spawn(3 * H)
+
+    def draw(i):
+        h, t = divmod(i, 3)
+        rng = np.random.default_rng(children[i])
+        x = out[t, h]
+        rng.standard_normal(size=(T, D), dtype=np.float32, out=x)
+        if kind == "outlier":
+            mask = rng.random(size=(T, D), dtype=np.float32) < 0.001
+            x[mask] = (10.0 * rng.standard_normal(size=int(mask.sum()), dtype=np.float32)).astype(np.float32)
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(draw, range(3 * H)))
+    return out[0], out[1], out[2]
 
 
 def generate_packed_workload(w: PackedWorkload):
