@@ -37,13 +37,16 @@ Modules
   varlen     packed variable-length documents: document-local blocks, attention
              inside each document, the work items and their longest-first
              order [P3 Abstract, 4.1 Performance on Packed Documents, 4.3]
+  decode     few new queries against an FP8 K/V cache: the E2 loop on key
+             ranges merged by their log-sum-exp, grouped query heads
+             [P1 Realistic applications]
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` to something
 other than itself (closed forms, an independent library, brute force,
 invariants).  Unpinned parts are listed in the functions that have them.
 """
 
-from . import e4m3, philox, hadamard, quantize, attention, fastexp, varlen  # noqa: F401
+from . import e4m3, philox, hadamard, quantize, attention, fastexp, varlen, decode  # noqa: F401
 from .attention import (  # noqa: F401
     attention_fp64,
     reference_attention,
