@@ -11,7 +11,8 @@ block scales applied by the scaled MFMA), the quantiser alone, the BF16 twin, th
 FP64 oracle on a bounded sample, the roofline of the attention kernel and the
 oracle's CPU throughput, and the packed variable-length document workloads
 (quantiser + attention with document-local scales, longest-first against
-document order).  Prints ONE JSON line.
+document order), and decode against an FP8 K/V cache (GB/s against the HBM
+peak).  Prints ONE JSON line.
 """
 
 import argparse
@@ -41,6 +42,7 @@ def parse():
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and accuracy sample")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length document workloads")
+    ap.add_argument("--no-decode", action="store_true", help="skip the FP8 K/V-cache decode workloads")
     ap.add_argument("--attn-only", action="store_true", help="time only attn_fp8_fwd launches (for profiling)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="with --attn-only: first run one plain device copy of this many MiB (counter calibration)")
@@ -265,10 +267,73 @@ def main():
 
     if not args.no_packed:
         result["packed_docs"] = packed_leg(args, fa, workloads, torch, dev, stream)
+    if not args.no_decode:
+        result["kv_decode"] = decode_leg(args, fa, workloads, torch, dev, stream)
     if not args.no_cpu:
         result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch, o_mx))
     print(json.dumps(result))
     return 0
+
+
+DECODE_NAMES = ("decode_gqa", "decode_gqa_spec")
+
+
+def decode_leg(args, fa, workloads, torch, dev, stream):
+    """Decode against an FP8 K/V cache: attn_fp8_decode (split kernel + merge)
+    with the cache and the new queries already quantised and resident in HBM.
+    HBM-bound: reported as the K/V cache bytes read per second and as all
+    algorithmic bytes (cache codes and descales, queries, partials written and
+    read back, outputs) per second against the 8 TB/s peak."""
+    import numpy as np
+    out = {}
+    for name in DECODE_NAMES:
+        w = workloads.DECODE_WORKLOADS[name]
+        q, k, v = (torch.from_numpy(x).to(dev) for x in workloads.generate_decode_workload(w))
+        _, k8, v8, _, kd, vd = fa.quantize_qkv_fp8(k, k, v, scale_block=w.scale_block, hadamard=w.hadamard,
+                                                   seed=w.sign_seed)
+        q8, _, _, qd, _, _ = fa.quantize_qkv_fp8(q, q, q, scale_block=w.scale_block, hadamard=w.hadamard,
+                                                 seed=w.sign_seed)
+        del q, k, v
+        sl_np = w.seqlens()
+        sl = torch.from_numpy(sl_np).to(dev)
+        split = fa.attn_fp8_decode_split(w.B, w.Hkv, w.Ncap, 0)
+        ws = torch.empty(fa.attn_fp8_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Ncap, w.D, 0),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+
+        def call():
+            fa.attn_fp8_decode(q8, qd, k8, v8, kd, vd, sl, scale_block=w.scale_block, hadamard=w.hadamard,
+                               causal=w.causal, out=(o, lse), workspace=ws)
+
+        for _ in range(5):
+            call()
+        n = max(20, args.steps)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(n):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        L = sl_np.astype(np.int64)
+        kv = w.kv_bytes()
+        nsplit = -(-w.Ncap // (4 * split))
+        mq = (w.Hq // w.Hkv) * w.Sq
+        total = (kv + 2 * 4 * w.Hkv * int((-(-L // w.scale_block)).sum()) + w.B * w.Hq * w.Sq * (w.D + 4)
+                 + 2 * w.B * w.Hkv * nsplit * mq * (w.D + 2) * 4 + w.B * w.Hq * w.Sq * (2 * w.D + 4))
+        out[name] = {
+            "workload": f"B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} D{w.D} cache {w.Ncap}, lengths "
+                        f"{int(L.min())}..{int(L.max())} (mean {int(L.mean())}), scale block {w.scale_block}",
+            "us": round(ms * 1e3, 2), "split": split,
+            "kv_cache_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
+            "algorithmic_gbs": round(total / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 2),
+        }
+        del q8, k8, v8, qd, kd, vd, ws
+    return out
 
 
 PACKED_NAMES = ("packed_skewed_causal", "packed_long_causal", "packed_equal_causal", "packed_skewed")

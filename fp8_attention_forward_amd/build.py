@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libattn_fp8.so")
-SOURCES = ["capi.hip", "quantize.hip", "attn_fp8.hip", "attn_bf16.hip", "varlen_schedule.hip"]
+SOURCES = ["capi.hip", "quantize.hip", "attn_fp8.hip", "attn_bf16.hip", "varlen_schedule.hip", "attn_decode.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,282 @@
+// Decode over an FP8 K/V cache (gfx950).
+//
+// "FP8 attention that keeps FlashAttention-3 throughput at BF16-level
+// accuracy", Realistic applications: storing K and V in FP8 relieves the
+// bandwidth of the KV cache.  A decode step reads every cached K and V byte
+// once for a handful of query rows (the Sq new tokens of the G query heads
+// that share one K/V head), so it is bound by HBM, not by the matrix cores:
+// at MQ = G * Sq <= 32 rows it does 4 * D * MQ FLOP per 2 * D bytes, a tenth
+// of the FP8 MFMA's FLOP-per-byte balance on MI355X.  The design therefore
+// goes for bytes in flight and full occupancy rather than for MFMA rate:
+//
+//   attn_fp8_decode_kernel: grid (splits, B * Hkv), 4 waves per workgroup.
+//     Wave w of split x owns the keys [(4 x + w) split, +split) of its
+//     sequence and runs the running-softmax loop of the dense kernel on them
+//     for all MQ rows (one 32-query MFMA column block; rows past MQ repeat
+//     row 0 and are dropped): K tiles go straight from HBM into the MFMA A
+//     layout (16-byte buffer loads; rows past the sequence read as zeros), V
+//     tiles through an 8 KiB LDS buffer of the wave so that the transpose
+//     read (ds_read_b64_tr_b8) can feed O^T += V^T P^T.  No workgroup barrier
+//     inside the loop: every wave streams on its own.  At the end the four
+//     waves merge in LDS by their log-sum-exp, in wave order, and write one
+//     partial (m, l, O unnormalised) per split.
+//   attn_fp8_decode_combine: one wave per output row merges the splits
+//     (M = max m, w = 2^(m - M), O = sum w O / sum w l), writes O in BF16 and
+//     LSE = ln 2 (M + log2 l).
+//
+// Numerics per key range are those of the dense kernel (scale folds, lazy
+// reference max, P = e4m3(2^(t - m) r_j) with r_j relative to the largest V
+// descale of the range, FP32 statistics).
+#include "common.h"
+#include "attn_internal.h"
+#include "fp8_tiles.h"
+
+namespace attnfp8 {
+
+template <int D, int SB, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p) {
+  using C = Fp8Cfg<D>;
+  static_assert(SB % kBC == 0, "a key tile lies in one scale block");
+  // V buffers during the loop, the merge after it
+  constexpr int kLdsBytes = (kWaves * C::TILE > (32 * D + 2 * kWaves * 32) * 4) ? kWaves * C::TILE
+                                                                                   : (32 * D + 2 * kWaves * 32) * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ql = lane & 31;
+  const int h = lane >> 5;
+  const int bk = blockIdx.y;                   // batch * Hkv + K/V head
+  const int b = bk / p.Hkv;
+  const int hk = bk - b * p.Hkv;
+  int L = p.seqlens[b];
+  L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
+  const int k0 = (blockIdx.x * kWaves + wave) * p.split;
+  const int k1 = L < k0 + p.split ? L : k0 + p.split;
+
+  // this lane's query row: r = g * Sq + i (query head hk * G + g, new token i)
+  const int r = ql < p.MQ ? ql : 0;
+  const int g = r / p.Sq;
+  const int i = r - g * p.Sq;
+  const int hq = hk * p.G + g;
+  const size_t qrow = ((size_t)b * p.Hq + hq) * p.Sq + i;
+  v8i qop[C::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) {
+    const v4i lo4 = *(const v4i*)(p.q8 + qrow * D + 64 * ks + 32 * h);
+    const v4i hi4 = *(const v4i*)(p.q8 + qrow * D + 64 * ks + 32 * h + 16);
+    qop[ks] = (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  }
+  const float c_q = p.qd[(size_t)b * p.Hq + hq] * p.score_scale;
+  const int qpos = L - p.Sq + i;               // position of this query in its sequence
+
+  const size_t kvh = (size_t)bk * p.Ncap * D;
+  const cfloat* kd = (const cfloat*)(p.kd + (size_t)bk * p.nblk);
+  const cfloat* vd = (const cfloat*)(p.vd + (size_t)bk * p.nblk);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8 + kvh), 0, L * D, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v8 + kvh), 0, L * D, 0x00020000);
+
+  // largest V descale over the blocks of this range (P carries r_j = dv_j / dvm)
+  float dvm = 1.0f;
+  if (k0 < k1) {
+    dvm = 0.0f;
+    for (int blk = k0 / SB; blk <= (k1 - 1) / SB; ++blk) dvm = fmaxf(dvm, vd[blk]);
+  }
+  const float log2_dvm = __builtin_amdgcn_logf(dvm);
+
+  const Fp8LaneOffsets<D> lo(lane);
+  uint8_t* vbuf = smem + wave * C::TILE;
+  v16f o[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = (v16f){};
+  float m_ref = -1e30f;
+  float l_acc = 0.0f;
+  v8i pop = (v8i){};
+
+  for (int t = k0; t < k1; t += kBC) {
+    // K operands straight into the A layout: row sub*32 + ql, bytes 64 ks + 32 h .. +31
+    KOps<D> kops;
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          kops.r[sub][ks][half] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, (t + sub * 32 + ql) * D + 64 * ks + 32 * h + 16 * half,
+                                                         0, 0));
+    // V tile into this wave's LDS buffer, 16-byte column slots swizzled per row
+#pragma unroll
+    for (int j = 0; j < C::CHUNKS; ++j) {
+      const int pos = j * 1024 + lane * 16;
+      const int row = pos / D;
+      const int slot = (pos % D) / 16;
+      const v4i val = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, t * D + pos, 0, 0));
+      *(v4i*)(vbuf + row * D + 16 * (slot ^ swz_v<D>(row))) = val;
+    }
+
+    // S^T = K Q^T
+    STile<D> s;
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) s[sub] = qk_mfma<D, false>(kops, qop, sub, 0, 0);
+    const int blk = t / SB;
+    const float c = c_q * kd[blk];
+    // keys past the range, and (causal) past this query's position
+    if (t + kBC > k1 || (CAUSAL && t + kBC - 1 > L - p.Sq)) {
+      const int lim = (CAUSAL ? (qpos < k1 - 1 ? qpos : k1 - 1) : k1 - 1) - t - 4 * h;
+#pragma unroll
+      for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          if (sub * 32 + 8 * (rr >> 2) + (rr & 3) > lim) s[sub][rr] = -INFINITY;
+    }
+    // statistics: lazy reference max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[sub][rr]);
+    float tmax = mx * c;
+    tmax = fmaxf(tmax, swap_halves(tmax));
+    const bool upd = tmax > m_ref + kTau;
+    const float m_new = upd ? tmax : m_ref;
+    const float alpha = upd ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+    m_ref = m_new;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
+    }
+    // P = 2^(t - m + log2 r) in e4m3 (B operand of the P V product), row sum of 2^(t - m)
+    const float dv = vd[blk];
+    const float inv_rv = dvm * __builtin_amdgcn_rcpf(dv);
+    const ExpArgs<kExpExact> ex(c, __builtin_amdgcn_logf(dv) - log2_dvm - m_ref);
+    float rs = 0.0f;
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float p0 = ex(s[sub][4 * a + 0]);
+        const float p1 = ex(s[sub][4 * a + 1]);
+        const float p2 = ex(s[sub][4 * a + 2]);
+        const float p3 = ex(s[sub][4 * a + 3]);
+        rs += (p0 + p1) + (p2 + p3);
+        int w = cvt_pk_fp8<false>(p0, p1, pop[4 * sub + a]);
+        w = cvt_pk_fp8<true>(p2, p3, w);
+        pop[4 * sub + a] = w;
+      }
+    l_acc = alpha * l_acc + rs * inv_rv;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      v2i part[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vbuf + 16 * rr * D + lo.v[dt]);
+      const v8i av = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+      o[dt] = mfma_f8x<false>(av, pop, o[dt], 0, 127);
+    }
+  }
+
+  // ---- merge the four waves by their log-sum-exp (in wave order), one partial per split
+  const float l_tot = l_acc + swap_halves(l_acc);
+  __syncthreads();                                   // every wave is done with its V buffer
+  float* mo = (float*)smem;                          // [32][D] merged O (unnormalised)
+  float* mm = mo + 32 * D;                           // [4][32] reference max of each wave
+  float* ml = mm + kWaves * 32;                      // [4][32] row sum of each wave
+  if (h == 0) {
+    mm[wave * 32 + ql] = m_ref;
+    ml[wave * 32 + ql] = l_tot;
+  }
+  __syncthreads();
+  float M = mm[ql];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mm[w * 32 + ql]);
+  float Lsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) Lsum += __builtin_amdgcn_exp2f(mm[w * 32 + ql] - M) * ml[w * 32 + ql];
+  const float f = __builtin_amdgcn_exp2f(m_ref - M) * dvm;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int idx = ql * D + 32 * dt + 8 * a + 4 * h + j;
+            const float v = f * o[dt][4 * a + j];
+            mo[idx] = w == 0 ? v : mo[idx] + v;
+          }
+    }
+    __syncthreads();
+  }
+  const size_t part = (size_t)bk * p.nsplit + blockIdx.x;
+  float* po = p.part_o + part * p.MQ * D;
+  for (int e = tid; e < p.MQ * D; e += 256) po[e] = mo[e];
+  if (tid < p.MQ) {
+    p.part_m[part * p.MQ + tid] = M;
+    p.part_l[part * p.MQ + tid] = Lsum;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
+  constexpr int PER = D / 64;                        // channels per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= p.B * p.Hkv * p.MQ) return;             // (no barrier in this kernel)
+  const int bk = row / p.MQ;
+  const int r = row - bk * p.MQ;
+  const int b = bk / p.Hkv;
+  const int hk = bk - b * p.Hkv;
+  const int g = r / p.Sq;
+  const int i = r - g * p.Sq;
+  const size_t base = (size_t)bk * p.nsplit;
+  float M = -INFINITY;
+  for (int x = 0; x < p.nsplit; ++x) M = fmaxf(M, p.part_m[(base + x) * p.MQ + r]);
+  float l = 0.0f;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+  for (int x = 0; x < p.nsplit; ++x) {
+    const float w = __builtin_amdgcn_exp2f(p.part_m[(base + x) * p.MQ + r] - M);
+    l += w * p.part_l[(base + x) * p.MQ + r];
+    const float* po = p.part_o + ((base + x) * p.MQ + r) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += w * po[lane + 64 * e];
+  }
+  const size_t orow = ((size_t)b * p.Hq + hk * p.G + g) * p.Sq + i;
+  const float inv_l = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const __bf16 v = (__bf16)(acc[e] * inv_l);
+    p.o[orow * D + lane + 64 * e] = __builtin_bit_cast(uint16_t, v);
+  }
+  if (lane == 0) p.lse[orow] = kLn2 * (M + __builtin_amdgcn_logf(l));
+}
+
+template <int D, int SB>
+static void launch_dec(const DecodeParams& p, int causal, hipStream_t stream) {
+  dim3 grid(p.nsplit, p.B * p.Hkv);
+  if (causal) attn_fp8_decode_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
+  else attn_fp8_decode_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
+}
+
+hipError_t launch_attn_fp8_decode(const DecodeParams& p, int D, int SB, int causal, hipStream_t stream) {
+  if (D == 64 && SB == 64) launch_dec<64, 64>(p, causal, stream);
+  else if (D == 64 && SB == 128) launch_dec<64, 128>(p, causal, stream);
+  else if (D == 128 && SB == 64) launch_dec<128, 64>(p, causal, stream);
+  else launch_dec<128, 128>(p, causal, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = p.B * p.Hkv * p.MQ;
+  dim3 cgrid((rows + kWaves - 1) / kWaves);
+  if (D == 64) attn_fp8_decode_combine<64><<<cgrid, 256, 0, stream>>>(p);
+  else attn_fp8_decode_combine<128><<<cgrid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace attnfp8

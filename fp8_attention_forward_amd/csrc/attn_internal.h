@@ -77,6 +77,35 @@ struct AttnFp8VarlenParams {
   float score_scale;
 };
 
+// Decode over an FP8 K/V cache: queries [B][Hq][Sq][D] (descales [B][Hq]),
+// cache codes [B][Hkv][Ncap][D] (descales [B][Hkv][nblk]), lengths [B].
+// Partials per (batch * Hkv, split): O [MQ][D], m [MQ], l [MQ].
+struct DecodeParams {
+  const uint8_t* q8;
+  const float* qd;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* kd;
+  const float* vd;
+  const int* seqlens;
+  float* part_o;
+  float* part_m;
+  float* part_l;
+  uint16_t* o;
+  float* lse;
+  int B;
+  int Hq;
+  int Hkv;
+  int G;           // query heads per K/V head
+  int Sq;          // new tokens per sequence
+  int MQ;          // G * Sq <= 32 query rows per K/V head
+  int Ncap;
+  int nblk;        // ceil(Ncap / scale_block)
+  int split;       // keys per wave range (multiple of 64)
+  int nsplit;      // ceil(Ncap / (4 * split)) partials per (batch, K/V head)
+  float score_scale;
+};
+
 struct AttnFp8Params {
   const uint8_t* q8;
   const uint8_t* k8;
@@ -120,6 +149,7 @@ hipError_t launch_varlen_schedule(const VarlenSchedParams& sp, hipStream_t strea
 // the schedule kernel, then the attention over H * m_cap workgroups (m_cap >= the item count)
 hipError_t launch_attn_fp8_varlen(const VarlenSchedParams& sp, const AttnFp8VarlenParams& p, int D, int SB, int causal,
                                   int exp_mode, int mx, int m_cap, hipStream_t stream);
+hipError_t launch_attn_fp8_decode(const DecodeParams& p, int D, int SB, int causal, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnBf16Params& p, int D, int causal, int BH, hipStream_t stream);
 
 }  // namespace attnfp8

@@ -282,6 +282,77 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                   "attn_fp8_fwd_varlen");
 }
 
+static int decode_split(int B, int Hkv, int Ncap, int split) {
+  if (split > 0) return split;
+  // the largest power of two in [64, 1024] keys per wave that still gives
+  // about four workgroups per CU (two resident at a time)
+  int s = 1024;
+  while (s > 64 && (long long)B * Hkv * ((Ncap + 4LL * s - 1) / (4LL * s)) < 1024) s /= 2;
+  return s;
+}
+
+size_t attn_fp8_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Ncap, int D, int split) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Ncap < 1 || D < 1 || split < 0 || Hq % Hkv) return 0;
+  const int s = decode_split(B, Hkv, Ncap, split);
+  const long long nsplit = (Ncap + 4LL * s - 1) / (4LL * s);
+  const long long mq = (long long)(Hq / Hkv) * Sq;
+  return (size_t)((long long)B * Hkv * nsplit * mq * (D + 2) * 4);
+}
+
+int attn_fp8_decode(const uint8_t* q8, const float* q_descale, const uint8_t* k8, const uint8_t* v8,
+                    const float* k_descale, const float* v_descale, const int32_t* seqlens, int B, int Hq, int Hkv,
+                    int Sq, int Ncap, int D, int scale_block, int hadamard, int causal, int split, void* workspace,
+                    size_t workspace_bytes, uint16_t* o_bf16, float* lse, void* stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Ncap < 1)
+    return fail(ATTN_EINVAL, "B, Hq, Hkv, Sq, Ncap must be >= 1 (got %d, %d, %d, %d, %d)", B, Hq, Hkv, Sq, Ncap);
+  if (D != 64 && D != 128) return fail(ATTN_EINVAL, "D must be 64 or 128 (got %d)", D);
+  CHECK(check_sb(scale_block));
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if ((Hq / Hkv) * Sq > 32) return fail(ATTN_EINVAL, "(Hq / Hkv) * Sq must be <= 32 (got %d)", (Hq / Hkv) * Sq);
+  if ((long long)Ncap * D >= (1LL << 30)) return fail(ATTN_EINVAL, "Ncap * D must be < 2^30");
+  if ((long long)B * Hkv > 65535) return fail(ATTN_EINVAL, "B * Hkv must be <= 65535");
+  if (split < 0 || split % 64 || split > 8192) return fail(ATTN_EINVAL, "split must be 0 or a multiple of 64 up to 8192");
+  if ((long long)B * Hq * Sq >= (1LL << 31)) return fail(ATTN_EINVAL, "B * Hq * Sq must be < 2^31");
+  CHECK(check_ptr(q8, 16, "q8"));
+  CHECK(check_ptr(q_descale, 4, "q_descale"));
+  CHECK(check_ptr(k8, 16, "k8"));
+  CHECK(check_ptr(v8, 16, "v8"));
+  CHECK(check_ptr(k_descale, 4, "k_descale"));
+  CHECK(check_ptr(v_descale, 4, "v_descale"));
+  CHECK(check_ptr(seqlens, 4, "seqlens"));
+  CHECK(check_ptr(workspace, 16, "workspace"));
+  CHECK(check_ptr(o_bf16, 16, "o_bf16"));
+  CHECK(check_ptr(lse, 4, "lse"));
+  const size_t need = attn_fp8_decode_workspace_bytes(B, Hq, Hkv, Sq, Ncap, D, split);
+  if (workspace_bytes < need)
+    return fail(ATTN_EINVAL, "workspace_bytes %zu < %zu (attn_fp8_decode_workspace_bytes)", workspace_bytes, need);
+  CHECK(check_device());
+  attnfp8::DecodeParams p;
+  p.q8 = q8; p.qd = q_descale;
+  p.k8 = k8; p.v8 = v8; p.kd = k_descale; p.vd = v_descale;
+  p.seqlens = seqlens;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.Sq = Sq; p.MQ = p.G * Sq;
+  p.Ncap = Ncap;
+  p.nblk = (Ncap + scale_block - 1) / scale_block;
+  p.split = decode_split(B, Hkv, Ncap, split);
+  p.nsplit = (Ncap + 4 * p.split - 1) / (4 * p.split);
+  const size_t nparts = (size_t)B * Hkv * p.nsplit * p.MQ;
+  p.part_o = (float*)workspace;
+  p.part_m = p.part_o + nparts * D;
+  p.part_l = p.part_m + nparts;
+  p.o = o_bf16; p.lse = lse;
+  double sc = 1.4426950408889634 / std::sqrt((double)D);
+  if (hadamard) sc /= D;
+  p.score_scale = (float)sc;
+  return launched(attnfp8::launch_attn_fp8_decode(p, D, scale_block, causal ? 1 : 0, (hipStream_t)stream),
+                  "attn_fp8_decode");
+}
+
+int attn_fp8_decode_split(int B, int Hkv, int Ncap, int split) {
+  if (B < 1 || Hkv < 1 || Ncap < 1 || split < 0) return 0;
+  return decode_split(B, Hkv, Ncap, split);
+}
+
 const char* attn_fp8_last_error(void) { return g_err; }
 
 int attn_fp8_abi_version(void) { return ATTN_FP8_ABI_VERSION; }

@@ -228,6 +228,56 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                         void* workspace, size_t workspace_bytes,
                         uint16_t* o_bf16, float* lse, void* stream);
 
+/* ---- Decode over an FP8 K/V cache ----------------------------------------
+ * "FP8 attention that keeps FlashAttention-3 throughput at BF16-level
+ * accuracy", Realistic applications: K and V stored in FP8 relieve the
+ * bandwidth of the KV cache.  A decode step attends the Sq newest tokens of
+ * each sequence to its cached keys; the cache moves one byte per element.
+ *
+ * Layout: cache codes k8, v8 [B][Hkv][Ncap][D] and descales
+ * [B][Hkv][ceil(Ncap / scale_block)] as quantize_qkv_fp8 writes them for the
+ * sequence (block b = tokens b*scale_block ..); sequence b uses its first
+ * L_b = seqlens[b] tokens, the Sq new ones included.  Queries q8
+ * [B][Hq][Sq][D] with q_descale [B][Hq] (quantize_qkv_fp8 on the new tokens:
+ * one block, Sq <= scale_block; rotated with the cache's seed when hadamard
+ * is set).  Query head h reads K/V head h / (Hq / Hkv) (grouped queries).
+ * Query i of sequence b sits at position L_b - Sq + i; causal: it sees keys
+ * up to that position.  Outputs o_bf16 [B][Hq][Sq][D], lse [B][Hq][Sq].
+ *
+ * The keys of a sequence are split into ranges of `split` keys (a multiple
+ * of 64; 0 = the library's choice, attn_fp8_decode_split); each range runs
+ * the loop of attn_fp8_fwd (P's V factor relative to the largest V descale
+ * of the range) and the ranges merge by their log-sum-exp.
+ * Sizes: (Hq / Hkv) * Sq <= 32 (so Sq <= scale_block), Ncap * D < 2^30,
+ * B * Hkv <= 65535.  seqlens: device int32 [B] with Sq <= L_b <= Ncap; other
+ * values give unspecified rows of that sequence (L_b is clamped to
+ * [0, Ncap], so every access stays in bounds).
+ */
+
+/* Keys per range used for `split` (0 = the library's choice: the largest
+ * power of two in [64, 1024] that still gives about 1024 workgroups). */
+int attn_fp8_decode_split(int B, int Hkv, int Ncap, int split);
+
+/* Bytes of device workspace attn_fp8_decode needs (the per-range partials):
+ * 4 * B * Hkv * ceil(Ncap / (4 * split')) * (Hq / Hkv) * Sq * (D + 2),
+ * split' = attn_fp8_decode_split(B, Hkv, Ncap, split); 0 for invalid sizes. */
+size_t attn_fp8_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Ncap, int D, int split);
+
+/* attn_fp8_decode -- FP8 attention of Sq new queries per sequence against an
+ * FP8 K/V cache.  Two launches on `stream`: the split kernel (one workgroup
+ * per 4 ranges of one (sequence, K/V head)) and the merge.
+ *   workspace : device memory, 16-byte aligned, caller-owned, at least
+ *               attn_fp8_decode_workspace_bytes(...) bytes; calls sharing a
+ *               workspace must not overlap.
+ * Other arguments as above; validation as for attn_fp8_fwd. */
+int attn_fp8_decode(const uint8_t* q8, const float* q_descale,
+                    const uint8_t* k8, const uint8_t* v8,
+                    const float* k_descale, const float* v_descale,
+                    const int32_t* seqlens, int B, int Hq, int Hkv, int Sq, int Ncap, int D,
+                    int scale_block, int hadamard, int causal, int split,
+                    void* workspace, size_t workspace_bytes,
+                    uint16_t* o_bf16, float* lse, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none).
  * The string is owned by the library and valid until the next call on that thread. */
 const char* attn_fp8_last_error(void);

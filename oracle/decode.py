@@ -33,16 +33,18 @@ import math
 import numpy as np
 
 from . import e4m3
-from .attention import round_to_bf16
+from .attention import e4m3_tie_step, round_to_bf16
 
 TILE = 64
 
 
 def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_block, hadamard, causal,
-                        split, tau=8.0, quantize_p=True, bf16_output=True):
+                        split, tau=8.0, quantize_p=True, bf16_output=True, tie_slack=False):
     """Decode of [B][Hq][Sq][D] query codes against the FP8 cache.  Returns
     (O [B][Hq][Sq][D], LSE [B][Hq][Sq]) in float64 (O rounded to BF16 values
-    unless ``bf16_output`` is False)."""
+    unless ``bf16_output`` is False) and, with ``tie_slack``, the movement of
+    O that valid lower-precision roundings of P allow (``attention.e4m3_tie_step``,
+    carried like O)."""
     if split % TILE or scale_block % TILE:
         raise ValueError("split and scale_block must be multiples of 64")
     B, Hq, Sq, D = np.shape(q8)
@@ -59,6 +61,7 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
     score_scale = math.log2(math.e) / math.sqrt(D) / (D if hadamard else 1)
     o = np.zeros((B, Hq, Sq, D))
     lse = np.zeros((B, Hq, Sq))
+    slack = np.zeros((B, Hq, Sq, D))
     for b in range(B):
         L = int(seqlens[b])
         if not Sq <= L <= np.shape(k8)[2]:
@@ -75,6 +78,7 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
                 m = np.full(Sq, -np.inf)
                 l = np.zeros(Sq)
                 acc = np.zeros((Sq, D))
+                slk = np.zeros((Sq, D))
                 for k0 in range(r0, r1, TILE):
                     k1 = min(r1, k0 + TILE)
                     blk = k0 // scale_block
@@ -91,17 +95,22 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
                     pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
                     pu[~ok] = 0.0
                     pq = pu * (vd[b, g, blk] / dv_ref)
+                    if tie_slack and quantize_p:
+                        slk = alpha[:, None] * slk + e4m3_tie_step(pq) @ np.abs(vv[b, g, k0:k1])
                     if quantize_p:
                         pq = e4m3.decode(e4m3.encode(pq))
                     l = alpha * l + pu.sum(axis=1)
                     acc = alpha[:, None] * acc + pq @ vv[b, g, k0:k1]
-                parts.append((m, l, acc * dv_ref))
+                parts.append((m, l, acc * dv_ref, slk * dv_ref))
             M = np.max([p[0] for p in parts], axis=0)
             w = [np.where(np.isfinite(p[0]), np.exp2(p[0] - M), 0.0) for p in parts]
             lt = sum(wi * p[1] for wi, p in zip(w, parts))
             ot = sum(wi[:, None] * p[2] for wi, p in zip(w, parts))
             o[b, h] = ot / lt[:, None]
             lse[b, h] = math.log(2.0) * (M + np.log2(lt))
+            slack[b, h] = sum(wi[:, None] * p[3] for wi, p in zip(w, parts)) / lt[:, None]
     if bf16_output:
         o = round_to_bf16(o)
+    if tie_slack:
+        return o, lse, slack
     return o, lse

@@ -215,6 +215,52 @@ def test_varlen_flags_and_workspace_size(lib):
         assert 16 + 8 * int(sum(-(-l // 128) for l in lens)) <= fa.attn_fp8_varlen_workspace_bytes(T, nd)
 
 
+def _dec(lib, **kw):
+    a = dict(q8=P, qd=P, k8=P, v8=P, kd=P, vd=P, sl=P, B=2, Hq=8, Hkv=2, Sq=1, Ncap=4096, D=128, sb=128, had=1,
+             causal=1, split=0, ws=P, wsb=1 << 30, o=P, lse=P)
+    a.update(kw)
+    return lib.attn_fp8_decode(a["q8"], a["qd"], a["k8"], a["v8"], a["kd"], a["vd"], a["sl"], a["B"], a["Hq"],
+                               a["Hkv"], a["Sq"], a["Ncap"], a["D"], a["sb"], a["had"], a["causal"], a["split"],
+                               a["ws"], a["wsb"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(B=0), ">= 1"),
+    (dict(Ncap=0), ">= 1"),
+    (dict(D=80), "D must be 64 or 128"),
+    (dict(sb=96), "scale_block"),
+    (dict(Hq=6, Hkv=4), "multiple of Hkv"),
+    (dict(Hq=64, Hkv=1), "<= 32"),
+    (dict(Hq=8, Hkv=2, Sq=9), "<= 32"),
+    (dict(Ncap=1 << 23), "Ncap * D"),
+    (dict(B=300, Hkv=300, Hq=300), "65535"),
+    (dict(split=100), "split"),
+    (dict(split=16384), "split"),
+    (dict(sl=NUL), "seqlens is NULL"),
+    (dict(ws=MIS), "workspace is not 16-byte aligned"),
+    (dict(wsb=16), "workspace_bytes"),
+    (dict(o=NUL), "o_bf16 is NULL"),
+])
+def test_attn_fp8_decode_rejects(lib, kw, frag):
+    assert _dec(lib, **kw) == fa.ATTN_EINVAL
+    assert frag in fa.last_error()
+
+
+def test_decode_split_and_workspace_size(lib):
+    # explicit splits pass through; the choice is a power of two in [64, 1024]
+    assert fa.attn_fp8_decode_split(2, 2, 4096, 192) == 192
+    for B, Hkv, N in ((1, 1, 100), (2, 8, 4096), (16, 8, 32768), (64, 8, 131072), (1, 1, 1 << 20)):
+        s = fa.attn_fp8_decode_split(B, Hkv, N)
+        assert s in (64, 128, 256, 512, 1024)
+        nsplit = -(-N // (4 * s))
+        assert B * Hkv * nsplit >= 1024 or s == 64
+        assert s == 1024 or B * Hkv * -(-N // (8 * s)) < 1024          # the largest such power of two
+    # partials: (D + 2) floats per (batch, K/V head, split, query row)
+    s = fa.attn_fp8_decode_split(2, 2, 4096)
+    assert fa.attn_fp8_decode_workspace_bytes(2, 8, 2, 1, 4096, 128) == 4 * 2 * 2 * -(-4096 // (4 * s)) * 4 * 130
+    assert fa.attn_fp8_decode_workspace_bytes(2, 8, 3, 1, 4096, 128) == 0
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(1, 1, 64, 64)

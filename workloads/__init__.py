@@ -208,3 +208,86 @@ def generate_packed(kind, H, T, D, seed):
 
 def generate_packed_workload(w: PackedWorkload):
     return generate_packed(w.kind, w.H, w.T, w.D, w.data_seed)
+
+
+# ---------------------------------------------------------------------------
+# Decode against an FP8 K/V cache ([P1] Realistic applications: FP8 K and V
+# relieve KV-cache bandwidth).  The pages give no decode workload; the stand-in
+# is a batch of sequences of mixed lengths with grouped query heads (G query
+# heads per K/V head), one new token each, head dimension 128.
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Ncap: int
+    D: int
+    causal: bool
+    scale_block: int
+    hadamard: bool
+    kind: str
+    data_seed: int
+    len_lo: int        # sequence lengths drawn uniformly from [len_lo, Ncap]
+    len_seed: int = 0
+    sign_seed: int = SIGN_SEED
+
+    def as_dict(self):
+        return asdict(self)
+
+    def seqlens(self):
+        rng = np.random.default_rng(self.len_seed)
+        return rng.integers(self.len_lo, self.Ncap + 1, size=self.B).astype(np.int32)
+
+    def kv_bytes(self):
+        """Bytes of K and V codes a decode step reads: 2 D per cached token and K/V head."""
+        return int(2 * self.D * self.Hkv * self.seqlens().astype(np.int64).sum())
+
+    def flops(self):
+        """4 d per visible (query, key) pair."""
+        L = self.seqlens().astype(np.int64)
+        pairs = (self.Sq * L - self.Sq * (self.Sq - 1) // 2) if self.causal else self.Sq * L
+        return int(4 * self.D * self.Hq * pairs.sum())
+
+
+DECODE_WORKLOADS = {
+    "decode_gqa": DecodeWorkload("decode_gqa", 16, 32, 8, 1, 32768, 128, True, 128, True, "iid", 7, 1024, 3),
+    "decode_gqa_spec": DecodeWorkload("decode_gqa_spec", 16, 32, 8, 4, 32768, 128, True, 128, True, "iid", 7, 1024, 3),
+}
+
+
+def generate_decode(kind, B, Hq, Hkv, Sq, Ncap, D, seed):
+    """(q [B, Hq, Sq, D], k [B, Hkv, Ncap, D], v [B, Hkv, Ncap, D]) float32.
+
+    Each (tensor, batch, head) slice has its own PCG64 stream, children of
+    SeedSequence(seed) in the order q slices, k slices, v slices (batch-major),
+    drawn as in ``generate_packed`` on several threads.
+    """
+    if kind not in ("iid", "outlier"):
+        raise ValueError(f"decode inputs support the iid and outlier kinds, not {kind!r}")
+    q = np.empty((B, Hq, Sq, D), dtype=np.float32)
+    k = np.empty((B, Hkv, Ncap, D), dtype=np.float32)
+    v = np.empty((B, Hkv, Ncap, D), dtype=np.float32)
+    slices = [(q, b, h) for b in range(B) for h in range(Hq)] + \
+        [(t, b, h) for t in (k, v) for b in range(B) for h in range(Hkv)]
+    children = np.random.SeedSequence(seed).spawn(len(slices))
+
+    def draw(j):
+        t, b, h = slices[j]
+        rng = np.random.default_rng(children[j])
+        x = t[b, h]
+        rng.standard_normal(size=x.shape, dtype=np.float32, out=x)
+        if kind == "outlier":
+            mask = rng.random(size=x.shape, dtype=np.float32) < 0.001
+            x[mask] = (10.0 * rng.standard_normal(size=int(mask.sum()), dtype=np.float32)).astype(np.float32)
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(draw, range(len(slices))))
+    return q, k, v
+
+
+def generate_decode_workload(w: DecodeWorkload):
+    return generate_decode(w.kind, w.B, w.Hq, w.Hkv, w.Sq, w.Ncap, w.D, w.data_seed)
