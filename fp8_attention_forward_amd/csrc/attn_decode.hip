@@ -15,14 +15,19 @@
 //     for all MQ rows (one 32-query MFMA column block; rows past MQ repeat
 //     row 0 and are dropped): K tiles go straight from HBM into the MFMA A
 //     layout (16-byte buffer loads; rows past the sequence read as zeros), V
-//     tiles through an 8 KiB LDS buffer of the wave so that the transpose
-//     read (ds_read_b64_tr_b8) can feed O^T += V^T P^T.  No workgroup barrier
-//     inside the loop: every wave streams on its own.  At the end the four
+//     tiles straight into an 8 KiB LDS buffer of the wave (buffer loads that
+//     write LDS) so that the transpose read (ds_read_b64_tr_b8) can feed
+//     O^T += V^T P^T.  No workgroup barrier inside the loop: every wave
+//     streams on its own, and three waves per SIMD hide each other's loads.  At the end the four
 //     waves merge in LDS by their log-sum-exp, in wave order, and write one
-//     partial (m, l, O unnormalised) per split.
+//     partial (m, l, O unnormalised) per split; splits past the sequence's
+//     end leave at once (lengths are known on the device only, so the grid
+//     covers the cache capacity).
 //   attn_fp8_decode_combine: one wave per output row merges the splits
 //     (M = max m, w = 2^(m - M), O = sum w O / sum w l), writes O in BF16 and
-//     LSE = ln 2 (M + log2 l).
+//     LSE = ln 2 (M + log2 l).  Maxima and weights are taken one split per
+//     lane; the O rows are then read with independent loads (no chain of
+//     dependent round trips through the splits).
 //
 // Numerics per key range are those of the dense kernel (scale folds, lazy
 // reference max, P = e4m3(2^(t - m) r_j) with r_j relative to the largest V
@@ -34,13 +39,12 @@
 namespace attnfp8 {
 
 template <int D, int SB, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 3) void attn_fp8_decode_kernel(DecodeParams p) {
   using C = Fp8Cfg<D>;
   static_assert(SB % kBC == 0, "a key tile lies in one scale block");
-  // V buffers during the loop, the merge after it
-  constexpr int kLdsBytes = (kWaves * C::TILE > (32 * D + 2 * kWaves * 32) * 4) ? kWaves * C::TILE
-                                                                                   : (32 * D + 2 * kWaves * 32) * 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  // a V buffer per wave during the loop, the merge after it (dynamic size:
+  // decode_lds_bytes)
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -52,6 +56,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
   const int hk = bk - b * p.Hkv;
   int L = p.seqlens[b];
   L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
+  // splits past the sequence's end hold no key: nothing to write (the merge
+  // reads only the splits below ceil(L / (4 split)))
+  if (blockIdx.x * kWaves * p.split >= L) return;
   const int k0 = (blockIdx.x * kWaves + wave) * p.split;
   const int k1 = L < k0 + p.split ? L : k0 + p.split;
 
@@ -73,20 +80,34 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
 
   const size_t kvh = (size_t)bk * p.Ncap * D;
   const cfloat* kd = (const cfloat*)(p.kd + (size_t)bk * p.nblk);
-  const cfloat* vd = (const cfloat*)(p.vd + (size_t)bk * p.nblk);
+  const cfloat* vd = (const cfloat*)(p.vd + (size_t)bk * p.nblk);   // (scalar loads in the loop)
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8 + kvh), 0, L * D, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v8 + kvh), 0, L * D, 0x00020000);
 
-  // largest V descale over the blocks of this range (P carries r_j = dv_j / dvm)
-  float dvm = 1.0f;
+  // largest V descale over the blocks of this range (P carries r_j = dv_j /
+  // dvm): one block per lane, then a wave maximum
+  float dvm = 0.0f;
   if (k0 < k1) {
-    dvm = 0.0f;
-    for (int blk = k0 / SB; blk <= (k1 - 1) / SB; ++blk) dvm = fmaxf(dvm, vd[blk]);
+    const int b0 = k0 / SB, b1 = (k1 - 1) / SB;
+    for (int blk = b0 + lane; blk <= b1; blk += 64) dvm = fmaxf(dvm, p.vd[(size_t)bk * p.nblk + blk]);
+    dvm = wave_max(dvm);
+  } else {
+    dvm = 1.0f;
   }
   const float log2_dvm = __builtin_amdgcn_logf(dvm);
 
   const Fp8LaneOffsets<D> lo(lane);
-  uint8_t* vbuf = smem + wave * C::TILE;
+  const uint8_t* vbuf0 = smem + wave * C::TILE;           // this wave's V buffer
+  const uint32_t vlds = lds_addr_of(vbuf0);
+  const v4i rsv = make_rsrc(p.v8 + kvh, (uint32_t)(L * D));
+  // buffer offset of the 16 bytes lane l moves into LDS chunk j: LDS (row,
+  // column slot c) holds source (row, c ^ swz_v(row)), as the transpose reads expect
+  int voff[C::CHUNKS];
+#pragma unroll
+  for (int j = 0; j < C::CHUNKS; ++j) {
+    const int pos = j * 1024 + lane * 16;
+    const int prow = pos / D;
+    voff[j] = prow * D + 16 * (((pos % D) / 16) ^ swz_v<D>(prow));
+  }
   v16f o[C::NDT];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) o[dt] = (v16f){};
@@ -94,32 +115,35 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
   float l_acc = 0.0f;
   v8i pop = (v8i){};
 
+  // Per tile: K straight into registers (compiler-tracked buffer loads), V
+  // straight into the wave's LDS buffer (buffer loads that write LDS, inline
+  // assembly: no registers held), one wait for both, then the tile's math.
+  // Registers stay low enough for three waves per SIMD, whose interleaving
+  // hides the load latency.
   for (int t = k0; t < k1; t += kBC) {
-    // K operands straight into the A layout: row sub*32 + ql, bytes 64 ks + 32 h .. +31
-    KOps<D> kops;
+    KOps<D> kc;
 #pragma unroll
     for (int sub = 0; sub < C::NSUB; ++sub)
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
-          kops.r[sub][ks][half] = __builtin_bit_cast(
+          kc.r[sub][ks][half] = __builtin_bit_cast(
               v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, (t + sub * 32 + ql) * D + 64 * ks + 32 * h + 16 * half,
                                                          0, 0));
-    // V tile into this wave's LDS buffer, 16-byte column slots swizzled per row
+    // (the previous tile's transpose reads of this buffer completed before
+    // its P V products issued)
 #pragma unroll
-    for (int j = 0; j < C::CHUNKS; ++j) {
-      const int pos = j * 1024 + lane * 16;
-      const int row = pos / D;
-      const int slot = (pos % D) / 16;
-      const v4i val = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, t * D + pos, 0, 0));
-      *(v4i*)(vbuf + row * D + 16 * (slot ^ swz_v<D>(row))) = val;
-    }
-
+    for (int j = 0; j < C::CHUNKS; ++j) buffer_to_lds16(rsv, t * D + voff[j], vlds + j * 1024);
+    // the builtin wait is seen by the compiler's own wait bookkeeping; the
+    // empty asm keeps the LDS reads below it
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __asm__ volatile("" ::: "memory");
+    const uint8_t* vcur = vbuf0;
     // S^T = K Q^T
     STile<D> s;
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) s[sub] = qk_mfma<D, false>(kops, qop, sub, 0, 0);
+    for (int sub = 0; sub < C::NSUB; ++sub) s[sub] = qk_mfma<D, false>(kc, qop, sub, 0, 0);
     const int blk = t / SB;
     const float c = c_q * kd[blk];
     // keys past the range, and (causal) past this query's position
@@ -173,18 +197,20 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
     for (int dt = 0; dt < C::NDT; ++dt) {
       v2i part[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vbuf + 16 * rr * D + lo.v[dt]);
+      for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
       const v8i av = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
       o[dt] = mfma_f8x<false>(av, pop, o[dt], 0, 127);
     }
   }
 
-  // ---- merge the four waves by their log-sum-exp (in wave order), one partial per split
+  // ---- merge the four waves by their log-sum-exp: waves 1..3 write their
+  // rows, scaled to the common maximum, into slabs of their own; wave 0 adds
+  // them to its own rows in wave order and writes the split's partial
   const float l_tot = l_acc + swap_halves(l_acc);
   __syncthreads();                                   // every wave is done with its V buffer
-  float* mo = (float*)smem;                          // [32][D] merged O (unnormalised)
-  float* mm = mo + 32 * D;                           // [4][32] reference max of each wave
+  float* mm = (float*)smem;                          // [4][32] reference max of each wave
   float* ml = mm + kWaves * 32;                      // [4][32] row sum of each wave
+  float* slab = ml + kWaves * 32;                    // [3][MQ][D] scaled O of waves 1..3
   if (h == 0) {
     mm[wave * 32 + ql] = m_ref;
     ml[wave * 32 + ql] = l_tot;
@@ -193,38 +219,49 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
   float M = mm[ql];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mm[w * 32 + ql]);
-  float Lsum = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) Lsum += __builtin_amdgcn_exp2f(mm[w * 32 + ql] - M) * ml[w * 32 + ql];
   const float f = __builtin_amdgcn_exp2f(m_ref - M) * dvm;
+  if (wave > 0 && ql < p.MQ) {
+    float* mine = slab + ((size_t)(wave - 1) * p.MQ + ql) * D;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(v4f*)(mine + 32 * dt + 8 * a + 4 * h) =
+            (v4f){f * o[dt][4 * a + 0], f * o[dt][4 * a + 1], f * o[dt][4 * a + 2], f * o[dt][4 * a + 3]};
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const size_t part = (size_t)bk * p.nsplit + blockIdx.x;
+    if (ql < p.MQ) {
+      float* po = p.part_o + (part * p.MQ + ql) * D;
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+          const int d = 32 * dt + 8 * a + 4 * h;
+          v4f acc = {f * o[dt][4 * a + 0], f * o[dt][4 * a + 1], f * o[dt][4 * a + 2], f * o[dt][4 * a + 3]};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int idx = ql * D + 32 * dt + 8 * a + 4 * h + j;
-            const float v = f * o[dt][4 * a + j];
-            mo[idx] = w == 0 ? v : mo[idx] + v;
+          for (int w = 1; w < kWaves; ++w) {
+            const v4f x = *(const v4f*)(slab + ((size_t)(w - 1) * p.MQ + ql) * D + d);
+            acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
           }
+          *(v4f*)(po + d) = acc;
+        }
+      if (h == 0) {
+        float Lsum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) Lsum += __builtin_amdgcn_exp2f(mm[w * 32 + ql] - M) * ml[w * 32 + ql];
+        p.part_m[part * p.MQ + ql] = M;
+        p.part_l[part * p.MQ + ql] = Lsum;
+      }
     }
-    __syncthreads();
-  }
-  const size_t part = (size_t)bk * p.nsplit + blockIdx.x;
-  float* po = p.part_o + part * p.MQ * D;
-  for (int e = tid; e < p.MQ * D; e += 256) po[e] = mo[e];
-  if (tid < p.MQ) {
-    p.part_m[part * p.MQ + tid] = M;
-    p.part_l[part * p.MQ + tid] = Lsum;
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
   constexpr int PER = D / 64;                        // channels per lane
+  constexpr int UNROLL = 8;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= p.B * p.Hkv * p.MQ) return;             // (no barrier in this kernel)
@@ -235,34 +272,74 @@ __global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
   const int g = r / p.Sq;
   const int i = r - g * p.Sq;
   const size_t base = (size_t)bk * p.nsplit;
+  int L = p.seqlens[b];
+  L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
+  const int nx = (L + kWaves * p.split - 1) / (kWaves * p.split);   // splits that hold keys
+  // the splits' maxima, one split per lane
   float M = -INFINITY;
-  for (int x = 0; x < p.nsplit; ++x) M = fmaxf(M, p.part_m[(base + x) * p.MQ + r]);
-  float l = 0.0f;
+  for (int x = lane; x < nx; x += 64) M = fmaxf(M, p.part_m[(base + x) * p.MQ + r]);
+  M = wave_max(M);
+  float lsum = 0.0f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int x = 0; x < p.nsplit; ++x) {
-    const float w = __builtin_amdgcn_exp2f(p.part_m[(base + x) * p.MQ + r] - M);
-    l += w * p.part_l[(base + x) * p.MQ + r];
-    const float* po = p.part_o + ((base + x) * p.MQ + r) * D;
+  for (int x0 = 0; x0 < nx; x0 += 64) {
+    // weights of 64 splits, one per lane, then O rows with independent loads
+    const int xl = x0 + lane;
+    float w = 0.0f;
+    if (xl < nx) {
+      w = __builtin_amdgcn_exp2f(p.part_m[(base + xl) * p.MQ + r] - M);
+      lsum += w * p.part_l[(base + xl) * p.MQ + r];
+    }
+    const int n = nx - x0 < 64 ? nx - x0 : 64;
+    int j = 0;
+    for (; j + UNROLL <= n; j += UNROLL) {
+      float vals[UNROLL][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * po[lane + 64 * e];
+      for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) vals[u][e] = p.part_o[((base + x0 + j + u) * p.MQ + r) * D + lane + 64 * e];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += wu * vals[u][e];
+      }
+    }
+    for (; j < n; ++j) {
+      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += wu * p.part_o[((base + x0 + j) * p.MQ + r) * D + lane + 64 * e];
+    }
   }
+  // row sum over the lanes
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) lsum += __shfl_xor(lsum, m, 64);
+  lsum += swap_halves(lsum);
   const size_t orow = ((size_t)b * p.Hq + hk * p.G + g) * p.Sq + i;
-  const float inv_l = 1.0f / l;
+  const float inv_l = 1.0f / lsum;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const __bf16 v = (__bf16)(acc[e] * inv_l);
     p.o[orow * D + lane + 64 * e] = __builtin_bit_cast(uint16_t, v);
   }
-  if (lane == 0) p.lse[orow] = kLn2 * (M + __builtin_amdgcn_logf(l));
+  if (lane == 0) p.lse[orow] = kLn2 * (M + __builtin_amdgcn_logf(lsum));
+}
+
+// LDS of the split kernel: the four V buffers, or the merge's maxima, sums
+// and three slabs, whichever is larger (at most 49 KiB)
+static size_t decode_lds_bytes(int D, int MQ) {
+  const size_t vbufs = (size_t)kWaves * kBC * D;
+  const size_t merge = (size_t)(2 * kWaves * 32 + (kWaves - 1) * MQ * D) * 4;
+  return vbufs > merge ? vbufs : merge;
 }
 
 template <int D, int SB>
 static void launch_dec(const DecodeParams& p, int causal, hipStream_t stream) {
   dim3 grid(p.nsplit, p.B * p.Hkv);
-  if (causal) attn_fp8_decode_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
-  else attn_fp8_decode_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
+  const size_t lds = decode_lds_bytes(D, p.MQ);
+  if (causal) attn_fp8_decode_kernel<D, SB, true><<<grid, 256, lds, stream>>>(p);
+  else attn_fp8_decode_kernel<D, SB, false><<<grid, 256, lds, stream>>>(p);
 }
 
 hipError_t launch_attn_fp8_decode(const DecodeParams& p, int D, int SB, int causal, hipStream_t stream) {

@@ -285,9 +285,12 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
 static int decode_split(int B, int Hkv, int Ncap, int split) {
   if (split > 0) return split;
   // the largest power of two in [64, 1024] keys per wave that still gives
-  // about four workgroups per CU (two resident at a time)
+  // 8192 workgroups over the cache capacity (32 per CU: sequences shorter
+  // than the capacity leave the rest empty, and every wave's chain of
+  // dependent tile loads stays short; measured best at 64-128 keys for
+  // 16 x 8 K/V heads of 32768)
   int s = 1024;
-  while (s > 64 && (long long)B * Hkv * ((Ncap + 4LL * s - 1) / (4LL * s)) < 1024) s /= 2;
+  while (s > 64 && (long long)B * Hkv * ((Ncap + 4LL * s - 1) / (4LL * s)) < 8192) s /= 2;
   return s;
 }
 

@@ -255,7 +255,7 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  */
 
 /* Keys per range used for `split` (0 = the library's choice: the largest
- * power of two in [64, 1024] that still gives about 1024 workgroups). */
+ * power of two in [64, 1024] that still gives 8192 workgroups over Ncap). */
 int attn_fp8_decode_split(int B, int Hkv, int Ncap, int split);
 
 /* Bytes of device workspace attn_fp8_decode needs (the per-range partials):

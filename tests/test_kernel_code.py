@@ -1,5 +1,5 @@
-"""Invariants of the generated gfx950 code of the FP8 attention kernel (CPU only:
-hipcc cross-compiles the source to assembly).
+"""Invariants of the generated gfx950 code of the FP8 attention kernels (CPU only:
+hipcc cross-compiles the sources to assembly).
 
 * Every tile / descale load that writes LDS directly is inline assembly that
   the compiler's hazard checks do not see; each must carry its own wait states
@@ -20,24 +20,37 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "fp8_attention_forward_amd", "csrc", "attn_fp8.hip")
+DECODE_SRC = os.path.join(ROOT, "fp8_attention_forward_amd", "csrc", "attn_decode.hip")
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
 
 pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 
 
-@pytest.fixture(scope="module")
-def kernels():
+def _compile(src, pattern):
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "--cuda-device-only", "-S", SRC, "-o", "-"]
+           "-packed-fp32-ops", "--cuda-device-only", "-S", src, "-o", "-"]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stderr[-2000:]
-    parts = re.split(r"\n(?=_ZN7attnfp8(?:15attn_fp8_kernel|22attn_fp8_varlen_kernel)\S*:)", res.stdout)
+    parts = re.split(r"\n(?=_ZN7attnfp8(?:" + pattern + r")\S*:)", res.stdout)
     funcs = {}
     for p in parts[1:]:
         name = p.split(":", 1)[0]
         funcs[name] = p.split("\n.Lfunc_end", 1)[0].splitlines()
+    return funcs
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    funcs = _compile(SRC, "15attn_fp8_kernel|22attn_fp8_varlen_kernel")
     # (dense, packed) x D x scale block x causal x exponential mode x MX
     assert len(funcs) == 64, sorted(funcs)
+    return funcs
+
+
+@pytest.fixture(scope="module")
+def decode_kernels():
+    funcs = _compile(DECODE_SRC, "22attn_fp8_decode_kernel")
+    assert len(funcs) == 8, sorted(funcs)   # D x scale block x causal
     return funcs
 
 
@@ -45,8 +58,8 @@ def _code(lines):
     return [l.strip() for l in lines if l.strip() and not l.strip().startswith(";")]
 
 
-def test_every_lds_dma_carries_its_wait_states(kernels):
-    for name, lines in kernels.items():
+def test_every_lds_dma_carries_its_wait_states(kernels, decode_kernels):
+    for name, lines in list(kernels.items()) + list(decode_kernels.items()):
         code = _code(lines)
         n = 0
         for i, ins in enumerate(code):
@@ -94,3 +107,18 @@ def test_partial_tile_waits_count_only_tile_loads(kernels):
             mem = [l.strip() for l in body if re.search(r"\b(scratch_|global_|flat_|buffer_store)", l)]
             assert not mem, f"{name} {lab}: compiler vector-memory operations in a loop with partial waits: {mem[:4]}"
         assert n_partial >= 1, name   # the main loop keeps loads in flight across steps
+
+
+def test_decode_waits_for_its_tile_loads_in_full(decode_kernels):
+    """The decode loop's V tiles arrive by LDS DMA that the compiler does not
+    count: the loop must wait for them with a full vmcnt(0) (seen by the
+    compiler) and keep no partial wait of its own, and must not spill."""
+    for name, lines in decode_kernels.items():
+        loops = [(lab, body) for lab, body in _loops(lines)
+                 if any(re.match(r"buffer_load_dword\S*\s.*\blds\b", l.strip()) for l in body)]
+        assert len(loops) == 1, name
+        _, body = loops[0]
+        waits = [l.strip() for l in body if l.strip().startswith("s_waitcnt") and "vmcnt" in l]
+        assert waits and all("vmcnt(0)" in w for w in waits), f"{name}: {waits}"
+        assert not _asm_blocks(body) or all(not w.startswith("s_waitcnt") for w in _asm_blocks(body))
+        assert not [l for l in body if "scratch_" in l], name
