@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and accuracy sample")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length document workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the FP8 K/V-cache decode workloads")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the decode workloads (for profiling); --copy-mb adds a calibration copy")
     ap.add_argument("--attn-only", action="store_true", help="time only attn_fp8_fwd launches (for profiling)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="with --attn-only: first run one plain device copy of this many MiB (counter calibration)")
@@ -86,8 +88,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.decode_only:
+        if args.copy_mb:
+            src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            src.fill_(1)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"mode": "decode_only",
+                          "kv_decode": decode_leg(args, fa, workloads, torch, dev, torch.cuda.current_stream(dev))}))
+        return 0
+    w = workloads.WORKLOADS[args.workload]
     q_np, k_np, v_np = workloads.generate_workload(w)
     q, k, v = (torch.from_numpy(x).to(dev) for x in (q_np, k_np, v_np))
     B, H, N, D, sb = w.B, w.H, w.N, w.D, w.scale_block
