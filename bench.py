@@ -30,7 +30,8 @@ METRIC = "FP8 attn fwd TFLOP/s (hd128, seq 8192) + RMSE vs FP64, ratio to BF16 R
 FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA
 BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["fp8_attention_forward_amd/csrc/attn_fp8.hip", "fp8_attention_forward_amd/csrc/common.h"]
+KERNEL_SOURCES = ["fp8_attention_forward_amd/csrc/attn_fp8.hip", "fp8_attention_forward_amd/csrc/fp8_tiles.h",
+                  "fp8_attention_forward_amd/csrc/attn_internal.h", "fp8_attention_forward_amd/csrc/common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fp8_outlier_traffic.json")
 
 
