@@ -77,7 +77,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every (batch, head) is independent; see the sharding note in DESIGN.md)", file=sys.stderr)
+              "(every (batch, head) is independent: heads shard across GPUs with no communication)", file=sys.stderr)
         return 2
 
     import numpy as np

@@ -134,7 +134,7 @@ def test_attn_fp8_matches_emulated_fp8(case):
 
 
 # Schraudolph's bit-level exponential (attn_fp8_fwd_opts, ATTN_FP8_EXP2_SCHRAUDOLPH)
-# against E2 with the same approximation: the benchmark spec's tolerance again.
+# against E2 with the same approximation: the same tolerance again.
 EXP2_CASES = [c for c in ATTN_CASES if not (c[7] == "channel" and not c[5])]
 
 
