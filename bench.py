@@ -163,7 +163,9 @@ def main():
     ms_step = total_ms / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in marks]
     attn_avg = sum(attn_ms) / len(attn_ms)
-    attn_med = sorted(attn_ms)[len(attn_ms) // 2]
+    srt = sorted(attn_ms)
+    attn_med = srt[len(srt) // 2]
+    attn_p10, attn_p90 = srt[len(srt) // 10], srt[min(len(srt) - 1, (9 * len(srt)) // 10)]
 
     # ---- quantiser alone (GB/s of algorithmic bytes: read 4 B, write 1 B per element, + descales)
     qs, qe = ev(), ev()
@@ -261,6 +263,8 @@ def main():
                    "B": B, "H": H, "N": N, "D": D, "causal": w.causal, "scale_block": sb,
                    "hadamard": w.hadamard, "quantisation": "included"},
         "attn_only": {"tflops": round(attn_tflops, 2), "ms_avg": round(attn_avg, 4), "ms_median": round(attn_med, 4),
+                      "ms_p10": round(attn_p10, 4), "ms_p90": round(attn_p90, 4),
+                      "tflops_median": round(flops / (attn_med * 1e-3) / 1e12, 2),
                       "frac_fp8_peak": round(attn_tflops / FP8_PEAK_TFLOPS, 4)},
         "quantiser": {"ms": round(quant_ms, 4), "gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                       "frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -275,7 +279,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic_for(w.name),
                      "algorithmic_bytes": attn_bytes, "kernel": "attn_fp8_kernel"},
+        "data_sha256": {nm: hashlib.sha256(np.ascontiguousarray(x).tobytes()).hexdigest()[:16]
+                        for nm, x in (("q", q_np), ("k", k_np), ("v", v_np))},
         "toolchain": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                      "numpy": np.__version__, "hipcc": hipcc_version(),
+                      "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
                       "device": torch.cuda.get_device_name(0)},
     }
 
@@ -414,6 +422,15 @@ def packed_leg(args, fa, workloads, torch, dev, stream):
     return out
 
 
+def hipcc_version():
+    import subprocess
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=20).stdout
+        return next((l.strip() for l in out.splitlines() if "HIP version" in l), None)
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
 def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu):
     """Oracle leg: time the FP64 reference on a bounded sample of the workload on
     the host cores and use the same reference rows for the accuracy report."""
@@ -435,6 +452,23 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu):
         if time.perf_counter() - t0 > 12.0:
             break
     cpu_s = time.perf_counter() - t0
+    # BLAS threads actually used, and one core alone on 1024 query rows of one head
+    blas_threads = None
+    single = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas_threads = max((i["num_threads"] for i in blas), default=None)
+        with threadpool_limits(1):
+            r1 = np.arange(1024)
+            t1 = time.perf_counter()
+            oatt.reference_attention(q_np[:1, :1], k_np[:1, :1], v_np[:1, :1], w.causal, rows=r1)
+            s1 = time.perf_counter() - t1
+        p1 = sum(int(r) + 1 for r in r1) if w.causal else len(r1) * w.N
+        single = {"gflops": round(4 * w.D * p1 / s1 / 1e9, 2), "sample": f"1 thread, 1024 query rows x {w.N} keys"}
+    except ImportError:
+        pass
+    used = cores if blas_threads is None else min(cores, blas_threads)
     if w.causal:
         pairs = sum(int(r) + 1 for r in rows)
     else:
@@ -465,8 +499,8 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu):
                      "fp8_schraudolph_rmse": rmses, "fp8_schraudolph_cosine": cos(es),
                      "fp8_mx_rmse": float(np.sqrt(np.mean(emx ** 2))), "fp8_mx_cosine": cos(emx),
                      "bound_ratio": 2.0, "rms_o": float(np.sqrt(np.mean(ra ** 2)))},
-        "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-                         "kind": "oracle",
+        "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": used,
+                         "kind": "oracle", "cores_available": cores, "single_thread": single,
                          "sample": f"FP64 exact attention (numpy BLAS) of {len(heads)} whole heads "
                                    f"({len(rows)} queries x {w.N} keys each), {cpu_s:.1f} s wall"},
     }
