@@ -160,16 +160,16 @@ __device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, 
 }
 
 // One pipelined step in two phases with the workgroup barrier between them.
-// On entry S_t (masked) and its statistics are ready and the K operands of
-// tile t+1 are in registers (read from LDS during the previous step).
-// Phase 1 issues the score MFMAs of tile t+1 in the same block as the
-// exponentials of tile t.  Phase 2 (after the barrier) reads V_t and the K
-// operands of tile t+2 from LDS and issues the P V MFMAs of tile t in the same
-// block as the statistics of tile t+1.
+// On entry S_t (masked) and its statistics are ready.  Phase A turns S_t into
+// P_t (exponentials, row sum, e4m3) after the O rescale that tile t asks for.
+// Phase B (after the barrier) adds V_t^T P_t^T to O and computes S_{t+1} =
+// K_{t+1} Q^T and its statistics; V and K operands are read from LDS right
+// before their MFMAs.  One score buffer serves both phases (S_t is dead once
+// P_t is packed), which keeps the registers low enough for three waves per
+// SIMD: the latency one wave waits on, the others fill.
 template <int D, int EXPM, bool MX>
-__device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const KOps<D>& k,
-                                           const v8i (&qop)[Fp8Cfg<D>::KSTEPS], Fp8State<D>& st, float c,
-                                           float inv_rv, float log2_rv, int sk_next, int sq) {
+__device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, float c, float inv_rv,
+                                           float log2_rv) {
   using C = Fp8Cfg<D>;
   // rescale O when some lane moved its reference max for tile t
   if (__builtin_amdgcn_ballot_w64(st.upd)) {
@@ -178,13 +178,12 @@ __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[dt][r] *= st.alpha;
   }
-  // S_{t+1} = K_{t+1} Q^T  ||  P_t = 2^(t - m + log2 r_t), row sum, e4m3
+  // P_t = 2^(t - m + log2 r_t), row sum, e4m3
   const ExpArgs<EXPM> ex(c, log2_rv - st.m_ref);
   float rs = 0.0f;
   v8i& pop = st.pop;
 #pragma unroll
-  for (int sub = 0; sub < C::NSUB; ++sub) {
-    s_next[sub] = qk_mfma<D, MX>(k, qop, sub, sk_next, sq);
+  for (int sub = 0; sub < C::NSUB; ++sub)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       float p0 = ex(s[sub][4 * a + 0]);
@@ -198,36 +197,42 @@ __device__ __forceinline__ void fp8_phase1(STile<D>& s, STile<D>& s_next, const 
       w = cvt_pk_fp8<true>(p2, p3, w);
       pop[4 * sub + a] = w;
     }
-  }
   st.l_acc = st.alpha * st.l_acc + rs * inv_rv;
-#pragma unroll
-  for (int i = 0; i < C::NSUB * C::KSTEPS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);   // then VALU work
-  }
 }
 
 template <int D, bool CAUSAL, bool MASK_NEXT, bool MX>
-__device__ __forceinline__ void fp8_phase2(STile<D>& s_next, const uint8_t* vcur, const uint8_t* knext2, KOps<D>& k,
-                                           const Fp8LaneOffsets<D>& lo, Fp8State<D>& st, int t, int N, int lane,
-                                           int iw, int my_q, float c_next, bool next_valid, int sv) {
+__device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, const uint8_t* knext,
+                                           const Fp8LaneOffsets<D>& lo, const v8i (&qop)[Fp8Cfg<D>::KSTEPS],
+                                           Fp8State<D>& st, int t, int N, int lane, int iw, int my_q, float c_next,
+                                           bool pv_active, bool next_valid, int sv, int sk_next, int sq) {
   using C = Fp8Cfg<D>;
-  // V_t^T operands first (the P V MFMAs wait for them), then the K operands
-  // of tile t+2 for the next step
-  v2i part[C::NDT][4];
+  if (!MASK_NEXT || pv_active) {
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt)
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      v2i part[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) part[dt][rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
-  read_k<D>(knext2, lo, k);
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) {
-    v8i a = {part[dt][0][0], part[dt][0][1], part[dt][1][0], part[dt][1][1],
-             part[dt][2][0], part[dt][2][1], part[dt][3][0], part[dt][3][1]};
-    st.o[dt] = mfma_f8x<MX>(a, st.pop, st.o[dt], sv, 127);
+      for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
+      const v8i a = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+      st.o[dt] = mfma_f8x<MX>(a, st.pop, st.o[dt], sv, 127);
+    }
   }
   // (a tile this wave will not visit must not move the reference max)
-  if (!MASK_NEXT || next_valid) tile_stats<D, CAUSAL, MASK_NEXT>(s_next, st, t + 1, N, lane, iw, my_q, c_next);
+  if (!MASK_NEXT || next_valid) {
+    // K operands one 32-key subtile at a time (16 registers in flight)
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) {
+      v16f acc = {};
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        const v4i a0 = lds_read_b128(knext + sub * 32 * D + lo.k[ks][0]);
+        const v4i a1 = lds_read_b128(knext + sub * 32 * D + lo.k[ks][1]);
+        const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        acc = mfma_f8x<MX>(a, qop[ks], acc, sk_next, sq);
+      }
+      s[sub] = acc;
+    }
+    tile_stats<D, CAUSAL, MASK_NEXT>(s, st, t + 1, N, lane, iw, my_q, c_next);
+  }
 }
 
 // One query tile (128 queries) of one sequence: the whole loop.  The view
@@ -287,6 +292,10 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
     const int last_w = (iw + kQueriesPerWave - 1 < N - 1) ? iw + kQueriesPerWave - 1 : N - 1;
     kt_w = last_w / kBC;
     n_clean = n_clean < i0 / kBC ? n_clean : i0 / kBC;
+  } else {
+    // (kept a run-time value: folded to n_kt - 1, it lets the compiler merge
+    // the tail into a form that no longer fits three waves per SIMD)
+    asm volatile("" : "+s"(kt_w));
   }
   // bytes of K / V this workgroup reads; loads past them return zeros
   const int rows_wg = N < n_kt_wg * kBC ? N : n_kt_wg * kBC;
@@ -321,38 +330,31 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   auto lr_of = [&](float dv) { return MX ? 0.0f : __builtin_amdgcn_logf(dv) - log2_dvm; };
   constexpr uint32_t KS = 0, VS = kRing * C::TILE;   // ring bases (byte offsets in smem)
 
-  // prologue: K0, K1, K2, V0 resident; S_0 and its statistics; K operands of
-  // tile 1 in registers; K3, V1 in flight (into K0's and a fresh V slot)
+  // prologue: K0, K1, K2, V0, V1 resident; S_0 and its statistics
   issue_tile<D, false>(kh8, lim, 0, KS + 0 * C::TILE, dma);
   issue_tile<D, false>(kh8, lim, 1, KS + 1 * C::TILE, dma);
   issue_tile<D, false>(kh8, lim, 2, KS + 2 * C::TILE, dma);
   issue_tile<D, true>(vh8, lim, 0, VS + 0 * C::TILE, dma);
+  issue_tile<D, true>(vh8, lim, 1, VS + 1 * C::TILE, dma);
   wait_vmem_all();
   __syncthreads();
-  STile<D> sa, sb;
-  qk_tile<D, MX>(smem + KS, lo, qop, sa, sk_of(0), sq);
+  STile<D> s;
+  qk_tile<D, MX>(smem + KS, lo, qop, s, sk_of(0), sq);
   st.alpha = 1.0f;
   st.upd = false;
-  tile_stats<D, CAUSAL, true>(sa, st, 0, N, lane, iw, my_q, c_of(0));
-  KOps<D> kops;
-  read_k<D>(smem + KS + 1 * C::TILE, lo, kops);
-  __syncthreads();   // K0 and K1 read by every wave: K0's slot may be refilled
-  issue_tile<D, false>(kh8, lim, 3, KS + 0 * C::TILE, dma);
-  issue_tile<D, true>(vh8, lim, 1, VS + 1 * C::TILE, dma);
+  tile_stats<D, CAUSAL, true>(s, st, 0, N, lane, iw, my_q, c_of(0));
 
-  // Step t: phase 1 (S_{t+1} MFMAs with the K operands in registers, P_t),
-  // then wait until only the previous step's loads are outstanding and
-  // barrier: K_{t+2} and V_t (issued two steps earlier) are now resident for
-  // every wave, and every wave has finished reading K_{t+1} and V_{t-1}.  The
-  // step issues K_{t+4} (into K_{t+1}'s slot) and V_{t+2} (into V_{t-1}'s
-  // slot), then runs phase 2.  S_t lives in sa for even t.
+  // Step t: phase A (P_t), then wait until only the previous step's loads are
+  // outstanding and barrier: K_{t+1} and V_t (issued two steps earlier) are
+  // now resident for every wave, and every wave has finished reading K_t and
+  // V_{t-1}.  The step issues K_{t+3} (into K_t's slot) and V_{t+2} (into
+  // V_{t-1}'s slot), then runs phase B.  Tile j lives in ring slot j % 3.
   //
   // Main loop: steps whose next tile needs no mask and is computed by every
-  // wave; ring slots are compile-time constants (unrolled over 6 = 3 slots x
-  // 2 score buffers).
+  // wave; ring slots are compile-time constants (unrolled over the 3 slots).
   const int t_main = n_clean - 1;
   int t = 0;
-#define FP8_MAIN(I, KR, KD, VC, VD, S1, S2)                                                            \
+#define FP8_STEP(I, KN, KF, VC, VF)                                                                   \
   {                                                                                                  \
     const int tt = t + (I);                                                                          \
     if (tt >= t_main) {                                                                              \
@@ -360,49 +362,37 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
       break;                                                                                         \
     }                                                                                                \
     const float dv = vd[tt / TPB];                                                                   \
-    fp8_phase1<D, EXPM, MX>(S1, S2, kops, qop, st, c_of(tt), ir_of(dv), lr_of(dv), sk_of(tt + 1), sq);   \
+    fp8_phaseA<D, EXPM, MX>(s, st, c_of(tt), ir_of(dv), lr_of(dv));                                  \
     wait_vmem_prev_step<2 * C::CHUNKS_PER_WAVE>();                                                   \
     workgroup_barrier();                                                                             \
-    issue_tile<D, false>(kh8, lim, tt + 4, KS + (KD) * C::TILE, dma);                                \
-    issue_tile<D, true>(vh8, lim, tt + 2, VS + (VD) * C::TILE, dma);                                 \
-    fp8_phase2<D, CAUSAL, false, MX>(S2, smem + VS + (VC) * C::TILE, smem + KS + (KR) * C::TILE, kops, lo, \
-                                     st, tt, N, lane, iw, my_q, c_of(tt + 1), true, sv_of(tt));       \
+    issue_tile<D, false>(kh8, lim, tt + 3, KS + (KF) * C::TILE, dma);                                \
+    issue_tile<D, true>(vh8, lim, tt + 2, VS + (VF) * C::TILE, dma);                                 \
+    fp8_phaseB<D, CAUSAL, false, MX>(s, smem + VS + (VC) * C::TILE, smem + KS + (KN) * C::TILE, lo, qop, st,   \
+                                     tt, N, lane, iw, my_q, c_of(tt + 1), true, true, sv_of(tt), sk_of(tt + 1), \
+                                     sq);                                                            \
   }
-  for (;; t += 6) {
-    FP8_MAIN(0, 2, 1, 0, 2, sa, sb)
-    FP8_MAIN(1, 0, 2, 1, 0, sb, sa)
-    FP8_MAIN(2, 1, 0, 2, 1, sa, sb)
-    FP8_MAIN(3, 2, 1, 0, 2, sb, sa)
-    FP8_MAIN(4, 0, 2, 1, 0, sa, sb)
-    FP8_MAIN(5, 1, 0, 2, 1, sb, sa)
+  for (;; t += 3) {
+    FP8_STEP(0, 1, 0, 0, 2)
+    FP8_STEP(1, 2, 1, 1, 0)
+    FP8_STEP(2, 0, 2, 2, 1)
   }
-#undef FP8_MAIN
+#undef FP8_STEP
 
-  // Tail (at most three steps): diagonal and ragged tiles, masks, and waves
-  // that stop early; ring slots computed at run time, S_t moved into sa.  The
-  // loads are waited for in full here (vmcnt(0)), so the wait stays correct
-  // whatever other memory operations the compiler schedules in this part.
-  if (t & 1) {
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) sa[sub] = sb[sub];
-  }
+  // Tail: diagonal and ragged tiles, masks, and waves that stop early; ring
+  // slots computed at run time.  The loads are waited for in full here
+  // (vmcnt(0)), so the wait stays correct whatever other memory operations the
+  // compiler schedules in this part.
   for (; t < n_kt_wg; ++t) {
     const bool active = t <= kt_w;
-    if (active) {
-      const float dv = vd[t / TPB];
-      fp8_phase1<D, EXPM, MX>(sa, sb, kops, qop, st, c_of(t), ir_of(dv), lr_of(dv), sk_of(t + 1), sq);
-    }
+    const float dv = vd[t / TPB];
+    if (active) fp8_phaseA<D, EXPM, MX>(s, st, c_of(t), ir_of(dv), lr_of(dv));
     wait_vmem_all();
     workgroup_barrier();
-    issue_tile<D, false>(kh8, lim, t + 4, KS + ((t + 1) % kRing) * C::TILE, dma);
+    issue_tile<D, false>(kh8, lim, t + 3, KS + (t % kRing) * C::TILE, dma);
     issue_tile<D, true>(vh8, lim, t + 2, VS + ((t + 2) % kRing) * C::TILE, dma);
-    if (active) {
-      fp8_phase2<D, CAUSAL, true, MX>(sb, smem + VS + (t % kRing) * C::TILE,
-                                      smem + KS + ((t + 2) % kRing) * C::TILE, kops, lo, st, t, N, lane, iw, my_q,
-                                      c_of(t + 1), t + 1 <= kt_w, sv_of(t));
-#pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub) sa[sub] = sb[sub];
-    }
+    fp8_phaseB<D, CAUSAL, true, MX>(s, smem + VS + (t % kRing) * C::TILE, smem + KS + ((t + 1) % kRing) * C::TILE,
+                                    lo, qop, st, t, N, lane, iw, my_q, c_of(t + 1), active, t + 1 <= kt_w, sv_of(t),
+                                    sk_of(t + 1), sq);
   }
   wait_vmem_all();   // no tile load may still be writing LDS when the workgroup ends
 
@@ -426,7 +416,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
 
 // Dense layout: one workgroup per (batch x head, query tile).
 template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
-__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
+__global__ __launch_bounds__(256, 3) void attn_fp8_kernel(AttnFp8Params p) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / p.n_qtiles;
   int qt = logical % p.n_qtiles;
@@ -453,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnFp8Params p) {
 // the 8 XCDs sends every item of a head to the same XCD when H is a multiple
 // of 8.  Workgroups past the item count leave before any barrier.
 template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
-__global__ __launch_bounds__(256, 2) void attn_fp8_varlen_kernel(AttnFp8VarlenParams p) {
+__global__ __launch_bounds__(256, 3) void attn_fp8_varlen_kernel(AttnFp8VarlenParams p) {
   const int e = blockIdx.x / p.H;
   const int h = blockIdx.x - e * p.H;
   if (e >= p.ws[0]) return;
