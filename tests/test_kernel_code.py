@@ -26,17 +26,37 @@ HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shut
 pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 
 
+_ASM = {}
+
+
+def _assembly(src):
+    if src not in _ASM:
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "--cuda-device-only", "-S", src, "-o", "-"]
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        assert res.returncode == 0, res.stderr[-2000:]
+        _ASM[src] = res.stdout
+    return _ASM[src]
+
+
 def _compile(src, pattern):
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "--cuda-device-only", "-S", src, "-o", "-"]
-    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
-    assert res.returncode == 0, res.stderr[-2000:]
-    parts = re.split(r"\n(?=_ZN7attnfp8(?:" + pattern + r")\S*:)", res.stdout)
+    parts = re.split(r"\n(?=_ZN7attnfp8(?:" + pattern + r")\S*:)", _assembly(src))
     funcs = {}
     for p in parts[1:]:
         name = p.split(":", 1)[0]
         funcs[name] = p.split("\n.Lfunc_end", 1)[0].splitlines()
     return funcs
+
+
+def _resources(src, names):
+    """Scratch bytes and waves per SIMD the compiler reports for each kernel."""
+    asm = _assembly(src)
+    out = {}
+    for name in names:
+        m = re.search(r"\.size\s+" + re.escape(name) + r",.*?; ScratchSize: (\d+).*?; Occupancy: (\d+)", asm, re.S)
+        assert m, name
+        out[name] = (int(m.group(1)), int(m.group(2)))
+    return out
 
 
 @pytest.fixture(scope="module")
@@ -45,6 +65,16 @@ def kernels():
     # (dense, packed) x D x scale block x causal x exponential mode x MX
     assert len(funcs) == 64, sorted(funcs)
     return funcs
+
+
+def test_attention_kernels_run_three_waves_per_simd_without_spills(kernels):
+    # the loop holds one score tile and reads K operands per subtile so that it
+    # fits in 168 VGPRs: three waves per SIMD (LDS: 48 KiB per workgroup, three
+    # workgroups per CU); a spill would also put compiler memory operations
+    # into the loop that waits with a partial vmcnt
+    for name, (scratch, occ) in _resources(SRC, kernels).items():
+        assert scratch == 0, f"{name}: {scratch} bytes of scratch"
+        assert occ >= 3, f"{name}: {occ} waves per SIMD"
 
 
 @pytest.fixture(scope="module")
