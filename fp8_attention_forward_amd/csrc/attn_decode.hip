@@ -9,20 +9,22 @@
 // of the FP8 MFMA's FLOP-per-byte balance on MI355X.  The design therefore
 // goes for bytes in flight and full occupancy rather than for MFMA rate:
 //
-//   attn_fp8_decode_kernel: grid (splits, B * Hkv), 4 waves per workgroup.
+//   attn_fp8_decode_kernel: grid (B * Hkv, splits), 4 waves per workgroup.
 //     Wave w of split x owns the keys [(4 x + w) split, +split) of its
 //     sequence and runs the running-softmax loop of the dense kernel on them
 //     for all MQ rows (one 32-query MFMA column block; rows past MQ repeat
 //     row 0 and are dropped): K tiles go straight from HBM into the MFMA A
 //     layout (16-byte buffer loads; rows past the sequence read as zeros), V
-//     tiles straight into an 8 KiB LDS buffer of the wave (buffer loads that
-//     write LDS) so that the transpose read (ds_read_b64_tr_b8) can feed
-//     O^T += V^T P^T.  No workgroup barrier inside the loop: every wave
-//     streams on its own, and three waves per SIMD hide each other's loads.  At the end the four
-//     waves merge in LDS by their log-sum-exp, in wave order, and write one
-//     partial (m, l, O unnormalised) per split; splits past the sequence's
-//     end leave at once (lengths are known on the device only, so the grid
-//     covers the cache capacity).
+//     tiles straight into one of two 8 KiB LDS buffers of the wave (buffer
+//     loads that write LDS) so that the transpose read (ds_read_b64_tr_b8)
+//     can feed O^T += V^T P^T.  Tile t+1's loads are in flight while tile t
+//     is computed; no workgroup barrier inside the loop: every wave streams
+//     on its own.  At the end the four waves merge in LDS by their
+//     log-sum-exp, in wave order, and write one partial (m, l, O
+//     unnormalised) per split.  The split index is the slow grid dimension:
+//     lengths are known on the device only, so the grid covers the cache
+//     capacity, and the splits past the shorter sequences' ends, dispatched
+//     last, leave at once.
 //   attn_fp8_decode_combine: one wave per output row merges the splits
 //     (M = max m, w = 2^(m - M), O = sum w O / sum w l), writes O in BF16 and
 //     LSE = ln 2 (M + log2 l).  Maxima and weights are taken one split per
@@ -39,11 +41,11 @@
 namespace attnfp8 {
 
 template <int D, int SB, bool CAUSAL>
-__global__ __launch_bounds__(256, 3) void attn_fp8_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p) {
   using C = Fp8Cfg<D>;
   static_assert(SB % kBC == 0, "a key tile lies in one scale block");
-  // a V buffer per wave during the loop, the merge after it (dynamic size:
-  // decode_lds_bytes)
+  // two V buffers per wave during the loop, the merge after it (dynamic
+  // size: decode_lds_bytes)
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -51,15 +53,19 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_decode_kernel(DecodeParams p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31;
   const int h = lane >> 5;
-  const int bk = blockIdx.y;                   // batch * Hkv + K/V head
+  // (the split index is the slow grid dimension: every sequence's first
+  // splits are dispatched before any later ones, so the splits past the
+  // shorter sequences' ends come last and leave while the others finish)
+  const int bk = blockIdx.x;                   // batch * Hkv + K/V head
+  const int xs = blockIdx.y;                   // split
   const int b = bk / p.Hkv;
   const int hk = bk - b * p.Hkv;
   int L = p.seqlens[b];
   L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
   // splits past the sequence's end hold no key: nothing to write (the merge
   // reads only the splits below ceil(L / (4 split)))
-  if (blockIdx.x * kWaves * p.split >= L) return;
-  const int k0 = (blockIdx.x * kWaves + wave) * p.split;
+  if (xs * kWaves * p.split >= L) return;
+  const int k0 = (xs * kWaves + wave) * p.split;
   const int k1 = L < k0 + p.split ? L : k0 + p.split;
 
   // this lane's query row: r = g * Sq + i (query head hk * G + g, new token i)
@@ -82,6 +88,42 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_decode_kernel(DecodeParams p)
   const cfloat* kd = (const cfloat*)(p.kd + (size_t)bk * p.nblk);
   const cfloat* vd = (const cfloat*)(p.vd + (size_t)bk * p.nblk);   // (scalar loads in the loop)
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8 + kvh), 0, L * D, 0x00020000);
+  const uint8_t* vbuf0 = smem + wave * 2 * C::TILE;       // this wave's two V buffers
+  const uint32_t vlds = lds_addr_of(vbuf0);
+  const v4i rsv = make_rsrc(p.v8 + kvh, (uint32_t)(L * D));
+  // buffer offset of the 16 bytes lane l moves into LDS chunk j: LDS (row,
+  // column slot c) holds source (row, c ^ swz_v(row)), as the transpose reads expect
+  int voff[C::CHUNKS];
+#pragma unroll
+  for (int j = 0; j < C::CHUNKS; ++j) {
+    const int pos = j * 1024 + lane * 16;
+    const int prow = pos / D;
+    voff[j] = prow * D + 16 * (((pos % D) / 16) ^ swz_v<D>(prow));
+  }
+  // K of a tile straight into the MFMA A layout (compiler-tracked buffer
+  // loads; rows past the sequence read as zeros), V into one of the wave's
+  // LDS buffers (buffer loads that write LDS, inline assembly: no registers)
+  KOps<D> kc;
+  auto load_k = [&](int t) {
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          kc.r[sub][ks][half] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, (t + sub * 32 + ql) * D + 64 * ks + 32 * h + 16 * half,
+                                                         0, 0));
+  };
+  auto load_v = [&](int t, int buf) {
+#pragma unroll
+    for (int j = 0; j < C::CHUNKS; ++j) buffer_to_lds16(rsv, t * D + voff[j], vlds + buf * C::TILE + j * 1024);
+  };
+  // the first tile's loads go out before the descale maximum is formed
+  if (k0 < k1) {
+    load_k(k0);
+    load_v(k0, 0);
+  }
 
   // largest V descale over the blocks of this range (P carries r_j = dv_j /
   // dvm): one block per lane, then a wave maximum
@@ -96,18 +138,6 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_decode_kernel(DecodeParams p)
   const float log2_dvm = __builtin_amdgcn_logf(dvm);
 
   const Fp8LaneOffsets<D> lo(lane);
-  const uint8_t* vbuf0 = smem + wave * C::TILE;           // this wave's V buffer
-  const uint32_t vlds = lds_addr_of(vbuf0);
-  const v4i rsv = make_rsrc(p.v8 + kvh, (uint32_t)(L * D));
-  // buffer offset of the 16 bytes lane l moves into LDS chunk j: LDS (row,
-  // column slot c) holds source (row, c ^ swz_v(row)), as the transpose reads expect
-  int voff[C::CHUNKS];
-#pragma unroll
-  for (int j = 0; j < C::CHUNKS; ++j) {
-    const int pos = j * 1024 + lane * 16;
-    const int prow = pos / D;
-    voff[j] = prow * D + 16 * (((pos % D) / 16) ^ swz_v<D>(prow));
-  }
   v16f o[C::NDT];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt) o[dt] = (v16f){};
@@ -115,35 +145,25 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_decode_kernel(DecodeParams p)
   float l_acc = 0.0f;
   v8i pop = (v8i){};
 
-  // Per tile: K straight into registers (compiler-tracked buffer loads), V
-  // straight into the wave's LDS buffer (buffer loads that write LDS, inline
-  // assembly: no registers held), one wait for both, then the tile's math.
-  // Registers stay low enough for three waves per SIMD, whose interleaving
-  // hides the load latency.
+  // Per tile t: one wait (tile t resident, and every transpose read of the
+  // other V buffer done), then V of tile t+1 into that buffer; the score
+  // products of tile t, then K of tile t+1 into the registers they have just
+  // read; then the softmax and the P V products of tile t.  A tile's loads
+  // thus overlap the whole previous tile, and no workgroup barrier is needed:
+  // every wave streams on its own.
   for (int t = k0; t < k1; t += kBC) {
-    KOps<D> kc;
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-          kc.r[sub][ks][half] = __builtin_bit_cast(
-              v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, (t + sub * 32 + ql) * D + 64 * ks + 32 * h + 16 * half,
-                                                         0, 0));
-    // (the previous tile's transpose reads of this buffer completed before
-    // its P V products issued)
-#pragma unroll
-    for (int j = 0; j < C::CHUNKS; ++j) buffer_to_lds16(rsv, t * D + voff[j], vlds + j * 1024);
-    // the builtin wait is seen by the compiler's own wait bookkeeping; the
-    // empty asm keeps the LDS reads below it
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // the builtin wait (vmcnt(0) lgkmcnt(0)) is seen by the compiler's own
+    // wait bookkeeping; the empty asm keeps memory operations on their side
+    __builtin_amdgcn_s_waitcnt(0x0070);
     __asm__ volatile("" ::: "memory");
-    const uint8_t* vcur = vbuf0;
+    const int par = ((t - k0) / kBC) & 1;
+    if (t + kBC < k1) load_v(t + kBC, par ^ 1);
+    const uint8_t* vcur = vbuf0 + par * C::TILE;
     // S^T = K Q^T
     STile<D> s;
 #pragma unroll
     for (int sub = 0; sub < C::NSUB; ++sub) s[sub] = qk_mfma<D, false>(kc, qop, sub, 0, 0);
+    if (t + kBC < k1) load_k(t + kBC);
     const int blk = t / SB;
     const float c = c_q * kd[blk];
     // keys past the range, and (causal) past this query's position
@@ -231,7 +251,7 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_decode_kernel(DecodeParams p)
   }
   __syncthreads();
   if (wave == 0) {
-    const size_t part = (size_t)bk * p.nsplit + blockIdx.x;
+    const size_t part = (size_t)bk * p.nsplit + xs;
     if (ql < p.MQ) {
       float* po = p.part_o + (part * p.MQ + ql) * D;
 #pragma unroll
@@ -326,17 +346,17 @@ __global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
   if (lane == 0) p.lse[orow] = kLn2 * (M + __builtin_amdgcn_logf(lsum));
 }
 
-// LDS of the split kernel: the four V buffers, or the merge's maxima, sums
-// and three slabs, whichever is larger (at most 49 KiB)
+// LDS of the split kernel: the eight V buffers, or the merge's maxima, sums
+// and three slabs, whichever is larger (at most 64 KiB)
 static size_t decode_lds_bytes(int D, int MQ) {
-  const size_t vbufs = (size_t)kWaves * kBC * D;
+  const size_t vbufs = (size_t)2 * kWaves * kBC * D;
   const size_t merge = (size_t)(2 * kWaves * 32 + (kWaves - 1) * MQ * D) * 4;
   return vbufs > merge ? vbufs : merge;
 }
 
 template <int D, int SB>
 static void launch_dec(const DecodeParams& p, int causal, hipStream_t stream) {
-  dim3 grid(p.nsplit, p.B * p.Hkv);
+  dim3 grid(p.B * p.Hkv, p.nsplit);
   const size_t lds = decode_lds_bytes(D, p.MQ);
   if (causal) attn_fp8_decode_kernel<D, SB, true><<<grid, 256, lds, stream>>>(p);
   else attn_fp8_decode_kernel<D, SB, false><<<grid, 256, lds, stream>>>(p);

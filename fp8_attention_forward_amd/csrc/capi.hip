@@ -285,12 +285,15 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
 static int decode_split(int B, int Hkv, int Ncap, int split) {
   if (split > 0) return split;
   // the largest power of two in [64, 1024] keys per wave that still gives
-  // 8192 workgroups over the cache capacity (32 per CU: sequences shorter
-  // than the capacity leave the rest empty, and every wave's chain of
-  // dependent tile loads stays short; measured best at 64-128 keys for
-  // 16 x 8 K/V heads of 32768)
+  // 1024 workgroups over the cache capacity (two rounds of the 512 the chip
+  // holds at two per CU when every sequence is full; shorter sequences leave
+  // their later splits empty).  Few long-lived workgroups stream best: each
+  // wave keeps a tile's loads in flight for its whole range, while every
+  // workgroup start and end costs dependent round trips (measured: 16 x 8
+  // K/V heads of 32768, lengths 2274..28617: 1024 keys per wave 89 us,
+  // 256 keys 97 us, 128 keys 101 us)
   int s = 1024;
-  while (s > 64 && (long long)B * Hkv * ((Ncap + 4LL * s - 1) / (4LL * s)) < 8192) s /= 2;
+  while (s > 64 && (long long)B * Hkv * ((Ncap + 4LL * s - 1) / (4LL * s)) < 1024) s /= 2;
   return s;
 }
 
@@ -315,6 +318,8 @@ int attn_fp8_decode(const uint8_t* q8, const float* q_descale, const uint8_t* k8
   if ((long long)Ncap * D >= (1LL << 30)) return fail(ATTN_EINVAL, "Ncap * D must be < 2^30");
   if ((long long)B * Hkv > 65535) return fail(ATTN_EINVAL, "B * Hkv must be <= 65535");
   if (split < 0 || split % 64 || split > 8192) return fail(ATTN_EINVAL, "split must be 0 or a multiple of 64 up to 8192");
+  if ((Ncap + 4LL * decode_split(B, Hkv, Ncap, split) - 1) / (4LL * decode_split(B, Hkv, Ncap, split)) > 65535)
+    return fail(ATTN_EINVAL, "ceil(Ncap / (4 * split)) must be <= 65535");
   if ((long long)B * Hq * Sq >= (1LL << 31)) return fail(ATTN_EINVAL, "B * Hq * Sq must be < 2^31");
   CHECK(check_ptr(q8, 16, "q8"));
   CHECK(check_ptr(q_descale, 4, "q_descale"));

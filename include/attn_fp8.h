@@ -249,13 +249,14 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  * the loop of attn_fp8_fwd (P's V factor relative to the largest V descale
  * of the range) and the ranges merge by their log-sum-exp.
  * Sizes: (Hq / Hkv) * Sq <= 32 (so Sq <= scale_block), Ncap * D < 2^30,
- * B * Hkv <= 65535.  seqlens: device int32 [B] with Sq <= L_b <= Ncap; other
+ * B * Hkv <= 65535, ceil(Ncap / (4 * split')) <= 65535.  seqlens: device int32 [B] with Sq <= L_b <= Ncap; other
  * values give unspecified rows of that sequence (L_b is clamped to
  * [0, Ncap], so every access stays in bounds).
  */
 
 /* Keys per range used for `split` (0 = the library's choice: the largest
- * power of two in [64, 1024] that still gives 8192 workgroups over Ncap). */
+ * power of two in [64, 1024] that still gives 1024 workgroups of four
+ * ranges over Ncap). */
 int attn_fp8_decode_split(int B, int Hkv, int Ncap, int split);
 
 /* Bytes of device workspace attn_fp8_decode needs (the per-range partials):
@@ -265,7 +266,8 @@ size_t attn_fp8_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Ncap,
 
 /* attn_fp8_decode -- FP8 attention of Sq new queries per sequence against an
  * FP8 K/V cache.  Two launches on `stream`: the split kernel (one workgroup
- * per 4 ranges of one (sequence, K/V head)) and the merge.
+ * per 4 ranges of one (sequence, K/V head); grid (B * Hkv, ranges / 4)) and
+ * the merge.
  *   workspace : device memory, 16-byte aligned, caller-owned, at least
  *               attn_fp8_decode_workspace_bytes(...) bytes; calls sharing a
  *               workspace must not overlap.

@@ -236,6 +236,7 @@ def _dec(lib, **kw):
     (dict(B=300, Hkv=300, Hq=300), "65535"),
     (dict(split=100), "split"),
     (dict(split=16384), "split"),
+    (dict(Ncap=(1 << 24) - 1, D=64, split=64), "65535"),          # split index is the grid's y dimension
     (dict(sl=NUL), "seqlens is NULL"),
     (dict(ws=MIS), "workspace is not 16-byte aligned"),
     (dict(wsb=16), "workspace_bytes"),
@@ -253,8 +254,9 @@ def test_decode_split_and_workspace_size(lib):
         s = fa.attn_fp8_decode_split(B, Hkv, N)
         assert s in (64, 128, 256, 512, 1024)
         nsplit = -(-N // (4 * s))
-        assert B * Hkv * nsplit >= 8192 or s == 64
-        assert s == 1024 or B * Hkv * -(-N // (8 * s)) < 8192          # the largest such power of two
+        assert B * Hkv * nsplit >= 1024 or s == 64
+        assert s == 1024 or B * Hkv * -(-N // (8 * s)) < 1024          # the largest such power of two
+    assert fa.attn_fp8_decode_split(16, 8, 32768) == 1024
     # partials: (D + 2) floats per (batch, K/V head, split, query row)
     s = fa.attn_fp8_decode_split(2, 2, 4096)
     assert fa.attn_fp8_decode_workspace_bytes(2, 8, 2, 1, 4096, 128) == 4 * 2 * 2 * -(-4096 // (4 * s)) * 4 * 130
