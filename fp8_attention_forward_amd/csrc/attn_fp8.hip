@@ -41,7 +41,10 @@
 //     exponent (so P stays <= 256), and the row sum divides it back out.
 //   * Lazy rescale: the reference max only moves when a tile's max exceeds it
 //     by more than kTau (log2 units), so most tiles skip the O rescale; P is
-//     then <= 2^kTau, inside e4m3's range.
+//     then <= 2^kTau, inside e4m3's range.  With exact exponentials P is
+//     formed first and the tile max is only taken when the row sum shows that
+//     the reference might have to move (the same decisions, without the max
+//     on most tiles).
 //   * Causal: key tiles past the workgroup's last query are not loaded, tiles
 //     past a wave's last query are not computed, masks only on diagonal and
 //     tail tiles; query tiles are scheduled longest first.
@@ -109,8 +112,6 @@ struct Fp8State {
   v16f o[Fp8Cfg<D>::NDT];
   float m_ref;     // reference max (log2 units)
   float l_acc;     // this lane's half of the row sum
-  float alpha;     // rescale factor of the tile about to be accumulated
-  bool upd;        // this lane moved its reference max for that tile
   v8i pop;         // P^T of the last tile in e4m3 (B operand of the P V product)
 };
 
@@ -128,12 +129,12 @@ struct Fp8SeqView {
   float score_scale;
 };
 
-// Mask + max + lazy reference update of a freshly computed score tile.
-// MASK = false: the tile is known to be complete and visible to every query
-// of the workgroup, and no mask code is emitted.
+// Mask of a freshly computed score tile: keys past the sequence, and (causal)
+// past each query's position, get -inf.  MASK = false: the tile is known to
+// be complete and visible to every query of the workgroup, and no code is
+// emitted.
 template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, int N, int lane, int iw, int my_q,
-                                           float c) {
+__device__ __forceinline__ void tile_mask(STile<D>& s, int t, int N, int lane, int iw, int my_q) {
   using C = Fp8Cfg<D>;
   const int h = lane >> 5;
   const int k0 = t * kBC;
@@ -146,42 +147,16 @@ __device__ __forceinline__ void tile_stats(STile<D>& s, Fp8State<D>& st, int t, 
       for (int r = 0; r < 16; ++r)
         if (sub * 32 + 8 * (r >> 2) + (r & 3) > lim) s[sub][r] = -INFINITY;
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-  float tmax = mx * c;              // c > 0: the max commutes with the scale
-  tmax = fmaxf(tmax, swap_halves(tmax));
-  st.upd = tmax > st.m_ref + kTau;
-  const float m_new = st.upd ? tmax : st.m_ref;
-  st.alpha = st.upd ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
-  st.m_ref = m_new;
 }
 
-// One pipelined step in two phases with the workgroup barrier between them.
-// On entry S_t (masked) and its statistics are ready.  Phase A turns S_t into
-// P_t (exponentials, row sum, e4m3) after the O rescale that tile t asks for.
-// Phase B (after the barrier) adds V_t^T P_t^T to O and computes S_{t+1} =
-// K_{t+1} Q^T and its statistics; V and K operands are read from LDS right
-// before their MFMAs.  One score buffer serves both phases (S_t is dead once
-// P_t is packed), which keeps the registers low enough for three waves per
-// SIMD: the latency one wave waits on, the others fill.
-template <int D, int EXPM, bool MX>
-__device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, float c, float inv_rv,
-                                           float log2_rv) {
+// P of one score tile against the reference max: P = 2^(t - m + log2 r) in
+// e4m3 into pop (the B operand of the P V product); returns this lane's
+// share of the row sum.
+template <int D, int EXPM>
+__device__ __forceinline__ float p_tile(const STile<D>& s, v8i& pop, float c, float bias) {
   using C = Fp8Cfg<D>;
-  // rescale O when some lane moved its reference max for tile t
-  if (__builtin_amdgcn_ballot_w64(st.upd)) {
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[dt][r] *= st.alpha;
-  }
-  // P_t = 2^(t - m + log2 r_t), row sum, e4m3
-  const ExpArgs<EXPM> ex(c, log2_rv - st.m_ref);
+  const ExpArgs<EXPM> ex(c, bias);
   float rs = 0.0f;
-  v8i& pop = st.pop;
 #pragma unroll
   for (int sub = 0; sub < C::NSUB; ++sub)
 #pragma unroll
@@ -197,13 +172,80 @@ __device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, f
       w = cvt_pk_fp8<true>(p2, p3, w);
       pop[4 * sub + a] = w;
     }
-  st.l_acc = st.alpha * st.l_acc + rs * inv_rv;
+  return rs;
+}
+
+// Lazy reference update from the tile maximum: the reference m moves only
+// when the tile's largest scaled score exceeds it by more than tau; then O is
+// rescaled by alpha = 2^(m_old - m_new) (1 for lanes that keep theirs).
+// Returns whether any lane of the wave moved.
+template <int D>
+__device__ __forceinline__ bool move_reference(const STile<D>& s, Fp8State<D>& st, float c, float& alpha) {
+  using C = Fp8Cfg<D>;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sub = 0; sub < C::NSUB; ++sub)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+  float tmax = mx * c;              // c > 0: the max commutes with the scale
+  tmax = fmaxf(tmax, swap_halves(tmax));
+  const bool upd = tmax > st.m_ref + kTau;
+  if (!__builtin_amdgcn_ballot_w64(upd)) return false;
+  const float m_new = upd ? tmax : st.m_ref;
+  alpha = upd ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
+  st.m_ref = m_new;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[dt][r] *= alpha;
+  return true;
+}
+
+// Largest normalised P (P / r <= 2^tau) the reference allows without moving,
+// less a margin for the rounding of the exponent argument (|m| < 2^14).
+constexpr float kMoveBound = 256.0f * (1.0f - 1.0f / 64.0f);
+
+// One pipelined step in two phases with the workgroup barrier between them.
+// On entry S_t (masked) is ready.  Phase A turns S_t into P_t (exponentials,
+// row sum, e4m3) with the lazy reference update that tile t asks for.
+// Phase B (after the barrier) adds V_t^T P_t^T to O and computes S_{t+1} =
+// K_{t+1} Q^T; V and K operands are read from LDS right before their MFMAs.
+// One score buffer serves both phases (S_t is dead once P_t is packed),
+// which keeps the registers low enough for three waves per SIMD: the latency
+// one wave waits on, the others fill.
+//
+// Exact exponentials: the reference moves only when some P_t / r_t would
+// exceed 2^tau against it, and the row sum bounds every P.  So P_t is formed
+// against the current reference first, and the tile maximum is taken only
+// when some lane's normalised row sum reaches kMoveBound (rarely once the
+// reference has settled; always on the first tile, whose reference is -1e30
+// and whose P overflow to +inf).  When the reference does move, P_t is formed
+// again, and each P is then at most r_t.  The decisions are those of taking
+// the maximum of every tile.  Schraudolph's exponential cannot be formed
+// first: past 2^128 its bits run into the sign field instead of saturating,
+// so there the maximum is taken before the exponentials, on every tile.
+template <int D, int EXPM, bool MX>
+__device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, float c, float inv_rv,
+                                           float log2_rv) {
+  float alpha = 1.0f;
+  float rs;
+  if constexpr (EXPM == kExpExact) {
+    rs = p_tile<D, EXPM>(s, st.pop, c, log2_rv - st.m_ref);
+    // (written so that a NaN sum also counts)
+    if (__builtin_amdgcn_ballot_w64(!(rs * inv_rv <= kMoveBound))) {
+      if (move_reference<D>(s, st, c, alpha)) rs = p_tile<D, EXPM>(s, st.pop, c, log2_rv - st.m_ref);
+    }
+  } else {
+    move_reference<D>(s, st, c, alpha);
+    rs = p_tile<D, EXPM>(s, st.pop, c, log2_rv - st.m_ref);
+  }
+  st.l_acc = alpha * st.l_acc + rs * inv_rv;
 }
 
 template <int D, bool CAUSAL, bool MASK_NEXT, bool MX>
 __device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, const uint8_t* knext,
                                            const Fp8LaneOffsets<D>& lo, const v8i (&qop)[Fp8Cfg<D>::KSTEPS],
-                                           Fp8State<D>& st, int t, int N, int lane, int iw, int my_q, float c_next,
+                                           Fp8State<D>& st, int t, int N, int lane, int iw, int my_q,
                                            bool pv_active, bool next_valid, int sv, int sk_next, int sq) {
   using C = Fp8Cfg<D>;
   if (!MASK_NEXT || pv_active) {
@@ -231,7 +273,7 @@ __device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, con
       }
       s[sub] = acc;
     }
-    tile_stats<D, CAUSAL, MASK_NEXT>(s, st, t + 1, N, lane, iw, my_q, c_next);
+    tile_mask<D, CAUSAL, MASK_NEXT>(s, t + 1, N, lane, iw, my_q);
   }
 }
 
@@ -330,7 +372,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   auto lr_of = [&](float dv) { return MX ? 0.0f : __builtin_amdgcn_logf(dv) - log2_dvm; };
   constexpr uint32_t KS = 0, VS = kRing * C::TILE;   // ring bases (byte offsets in smem)
 
-  // prologue: K0, K1, K2, V0, V1 resident; S_0 and its statistics
+  // prologue: K0, K1, K2, V0, V1 resident; S_0 (masked)
   issue_tile<D, false>(kh8, lim, 0, KS + 0 * C::TILE, dma);
   issue_tile<D, false>(kh8, lim, 1, KS + 1 * C::TILE, dma);
   issue_tile<D, false>(kh8, lim, 2, KS + 2 * C::TILE, dma);
@@ -340,9 +382,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   __syncthreads();
   STile<D> s;
   qk_tile<D, MX>(smem + KS, lo, qop, s, sk_of(0), sq);
-  st.alpha = 1.0f;
-  st.upd = false;
-  tile_stats<D, CAUSAL, true>(s, st, 0, N, lane, iw, my_q, c_of(0));
+  tile_mask<D, CAUSAL, true>(s, 0, N, lane, iw, my_q);
 
   // Step t: phase A (P_t), then wait until only the previous step's loads are
   // outstanding and barrier: K_{t+1} and V_t (issued two steps earlier) are
@@ -368,8 +408,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
     issue_tile<D, false>(kh8, lim, tt + 3, KS + (KF) * C::TILE, dma);                                \
     issue_tile<D, true>(vh8, lim, tt + 2, VS + (VF) * C::TILE, dma);                                 \
     fp8_phaseB<D, CAUSAL, false, MX>(s, smem + VS + (VC) * C::TILE, smem + KS + (KN) * C::TILE, lo, qop, st,   \
-                                     tt, N, lane, iw, my_q, c_of(tt + 1), true, true, sv_of(tt), sk_of(tt + 1), \
-                                     sq);                                                            \
+                                     tt, N, lane, iw, my_q, true, true, sv_of(tt), sk_of(tt + 1), sq);       \
   }
   for (;; t += 3) {
     FP8_STEP(0, 1, 0, 0, 2)
@@ -391,8 +430,8 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
     issue_tile<D, false>(kh8, lim, t + 3, KS + (t % kRing) * C::TILE, dma);
     issue_tile<D, true>(vh8, lim, t + 2, VS + ((t + 2) % kRing) * C::TILE, dma);
     fp8_phaseB<D, CAUSAL, true, MX>(s, smem + VS + (t % kRing) * C::TILE, smem + KS + ((t + 1) % kRing) * C::TILE,
-                                    lo, qop, st, t, N, lane, iw, my_q, c_of(t + 1), active, t + 1 <= kt_w, sv_of(t),
-                                    sk_of(t + 1), sq);
+                                    lo, qop, st, t, N, lane, iw, my_q, active, t + 1 <= kt_w, sv_of(t), sk_of(t + 1),
+                                    sq);
   }
   wait_vmem_all();   // no tile load may still be writing LDS when the workgroup ends
 
@@ -418,8 +457,10 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
 template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
 __global__ __launch_bounds__(256, 3) void attn_fp8_kernel(AttnFp8Params p) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / p.n_qtiles;
-  int qt = logical % p.n_qtiles;
+  // (the division runs on the vector ALU: bring the uniform results back to
+  // scalar registers, so that every address derived from them stays scalar)
+  const int bh = __builtin_amdgcn_readfirstlane(logical / p.n_qtiles);
+  int qt = __builtin_amdgcn_readfirstlane(logical - bh * p.n_qtiles);
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;            // longest tiles first
   const size_t head = (size_t)bh * p.N * D;
   Fp8SeqView seq;
@@ -444,7 +485,7 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_kernel(AttnFp8Params p) {
 // of 8.  Workgroups past the item count leave before any barrier.
 template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
 __global__ __launch_bounds__(256, 3) void attn_fp8_varlen_kernel(AttnFp8VarlenParams p) {
-  const int e = blockIdx.x / p.H;
+  const int e = __builtin_amdgcn_readfirstlane(blockIdx.x / p.H);   // (uniform: scalar loads below)
   const int h = blockIdx.x - e * p.H;
   if (e >= p.ws[0]) return;
   const int2 item = ((const int2*)(p.ws + kWsHeaderInts))[e];

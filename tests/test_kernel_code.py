@@ -100,13 +100,25 @@ def test_every_lds_dma_carries_its_wait_states(kernels, decode_kernels):
 
 
 def _loops(lines):
-    """(label, body lines) of every loop: from its header to its last back edge."""
+    """(label, body lines) of every loop: its header block and every block the
+    compiler annotates as inside it ("in Loop: Header=..."; loops entered by
+    fall-through have no branch to their header, so the annotations are the
+    reliable record)."""
+    starts = [i for i, l in enumerate(lines) if re.match(r"^\.LBB\S+:", l)]
+    blocks = []
+    for k, st in enumerate(starts):
+        end = starts[k + 1] if k + 1 < len(starts) else len(lines)
+        blocks.append((lines[st].split(":", 1)[0], st, end, lines[st]))
     out = []
-    for i, l in enumerate(lines):
-        if "Loop Header" in l:
-            lab = l.split(":", 1)[0]
-            back = [j for j, m in enumerate(lines) if re.search(r"s_c?branch\S*\s+" + re.escape(lab) + r"\s*$", m)]
-            out.append((lab, lines[i:max(back) + 1]))
+    for lab, st, end, head in blocks:
+        if "Loop Header" not in head:
+            continue
+        hdr = lab[1:].replace("LBB", "BB", 1)           # annotations name .LBB0_13 as BB0_13
+        body = []
+        for lab2, st2, end2, head2 in blocks:
+            if lab2 == lab or re.search(r"in Loop: Header=" + re.escape(hdr) + r"\b", head2):
+                body += lines[st2:end2]
+        out.append((lab, body))
     return out
 
 
