@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode workloads (for profiling); --copy-mb adds a calibration copy")
     ap.add_argument("--attn-only", action="store_true", help="time only attn_fp8_fwd launches (for profiling)")
+    ap.add_argument("--bf16", action="store_true", help="with --attn-only: time the BF16 twin's launches instead")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="with --attn-only: first run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -130,17 +131,24 @@ def main():
             torch.cuda.synchronize()
             dst.copy_(src)
             torch.cuda.synchronize()
-        quant()
+        run = attn
+        if args.bf16:
+            # (inputs cast to BF16 before the timed launches)
+            qb, kb, vb = (x.to(torch.bfloat16) for x in (q, k, v))
+            ob, lb = torch.empty_like(o), torch.empty_like(lse)
+            run = lambda: fa.attn_bf16_fwd(qb, kb, vb, causal=w.causal, out=(ob, lb))
+        else:
+            quant()
         for _ in range(args.warmup):
-            attn()
+            run()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            attn()
+            run()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        print(json.dumps({"mode": "attn_only", "workload": w.name, "ms_per_launch": ms,
-                          "tflops": flops / (ms * 1e-3) / 1e12}))
+        print(json.dumps({"mode": "attn_only", "kernel": "attn_bf16_fwd" if args.bf16 else "attn_fp8_fwd",
+                          "workload": w.name, "ms_per_launch": ms, "tflops": flops / (ms * 1e-3) / 1e12}))
         return 0
 
     # ---- timed region: K steps of quantise + attention, events around each attention launch
