@@ -34,10 +34,24 @@ struct Bf16Cfg {
   static_assert(CHUNKS % kWaves == 0, "tile must split evenly over the waves");
 };
 
+// XOR swizzles of the 16-byte column slot per LDS row, for 64 banks of 4 bytes
+// (256 bytes per bank cycle; a D = 128 row is one full cycle, a D = 64 row half
+// of one).  They keep every slot inside its row, and the loader applies the
+// same function, so a read of logical slot s at slot s ^ swz(row) finds it.
+//   K (ds_read_b128, 16 lanes per cycle, one row per lane): any 16 consecutive
+//     rows at one logical slot land in 16 distinct 16-byte bank groups.
+//   V (ds_read_b64_tr_b16, 32 lanes per cycle: 4 consecutive rows x 4 slots of
+//     one d-tile): the 4 rows' slot groups are disjoint.
 template <int D>
-__device__ __forceinline__ int swz_k16(int row) { return row & 7; }
+__device__ __forceinline__ int swz_k16(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
 template <int D>
-__device__ __forceinline__ int swz_v16(int row) { return 2 * (row & 3); }
+__device__ __forceinline__ int swz_v16(int row) {
+  if constexpr (D == 128) return 4 * (row & 3);
+  else return 2 * (row & 3);
+}
 
 template <int D, bool IS_V>
 __device__ __forceinline__ void load_tile16(const uint16_t* __restrict__ src, uint8_t* buf, int kt, int N,
