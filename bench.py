@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and accuracy sample")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length document workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the FP8 K/V-cache decode workloads")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the causal, ablation-shape and channel-outlier configurations")
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode workloads (for profiling); --copy-mb adds a calibration copy")
     ap.add_argument("--attn-only", action="store_true", help="time only attn_fp8_fwd launches (for profiling)")
@@ -299,10 +301,127 @@ def main():
         result["packed_docs"] = packed_leg(args, fa, workloads, torch, dev, stream)
     if not args.no_decode:
         result["kv_decode"] = decode_leg(args, fa, workloads, torch, dev, stream)
+    samples = []
+    if not args.no_configs:
+        result["configs"], samples = configs_leg(args, fa, workloads, torch, dev, stream, w, (q, k, v), q_np, k_np,
+                                                 v_np)
     if not args.no_cpu:
         result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch, o_mx))
+        if samples:
+            config_accuracy(result["configs"], samples)
     print(json.dumps(result))
     return 0
+
+
+CONFIG_NAMES = ("outlier_causal", "ablation", "channel", "channel_norot")
+
+
+def configs_leg(args, fa, workloads, torch, dev, stream, w0, dev0, q0_np, k0_np, v0_np):
+    """The other configurations of the metric: the outlier workload made causal
+    (the same tensors), the ablation shape (FP8 path against the BF16 twin), and
+    channel outliers with and without the rotation.  Per configuration: one step
+    (quantise + attention) and the attention alone, median of per-launch HIP
+    events, inputs resident in HBM; the BF16 twin where the configuration
+    compares against it.  Returns the timings and, for the accuracy report, the
+    FP8 / BF16 outputs of two heads on a fixed sample of query rows."""
+    import numpy as np
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out, samples = {}, []
+    cache = {}
+    for name in CONFIG_NAMES:
+        w = workloads.WORKLOADS[name]
+        key = (w.kind, w.B, w.H, w.N, w.D, w.data_seed)
+        if key == (w0.kind, w0.B, w0.H, w0.N, w0.D, w0.data_seed):
+            arrs, (q, k, v) = (q0_np, k0_np, v0_np), dev0
+        else:
+            if key not in cache:
+                cache.clear()
+                a = workloads.generate_workload(w)
+                cache[key] = (a, tuple(torch.from_numpy(x).to(dev) for x in a))
+            arrs, (q, k, v) = cache[key]
+        B, H, N, D, sb = w.B, w.H, w.N, w.D, w.scale_block
+        nb = -(-N // sb)
+        q8, k8, v8 = (torch.empty((B, H, N, D), dtype=torch.uint8, device=dev) for _ in range(3))
+        qd, kd, vd = (torch.empty((B, H, nb), dtype=torch.float32, device=dev) for _ in range(3))
+        o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+        def quant():
+            fa.quantize_qkv_fp8(q, k, v, scale_block=sb, hadamard=w.hadamard, seed=w.sign_seed,
+                                out=(q8, k8, v8, qd, kd, vd))
+
+        def attn():
+            fa.attn_fp8_fwd(q8, k8, v8, qd, kd, vd, scale_block=sb, hadamard=w.hadamard, causal=w.causal,
+                            out=(o, lse))
+
+        def timed(fn, n):
+            for _ in range(3):
+                fn()
+            marks = [(ev(), ev()) for _ in range(n)]
+            torch.cuda.synchronize()
+            for a, b in marks:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in marks]))
+
+        n = max(10, args.steps // 4)
+        step_ms = timed(lambda: (quant(), attn()), n)
+        attn_ms = timed(attn, n)
+        flops = w.flops()
+        r = {"workload": f"{name}: B{B} H{H} N{N} D{D} {'causal' if w.causal else 'non-causal'}, scale block {sb}, "
+                         f"rotation {'on' if w.hadamard else 'off'}, {w.kind} inputs",
+             "step_ms": round(step_ms, 4), "tflops_step": round(flops / (step_ms * 1e-3) / 1e12, 2),
+             "attn_ms": round(attn_ms, 4), "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
+             "attn_frac_fp8_peak": round(flops / (attn_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        ob = None
+        if name != "channel_norot":
+            qb, kb, vb = (x.to(torch.bfloat16) for x in (q, k, v))
+            ob, lb = torch.empty_like(o), torch.empty_like(lse)
+            bf_ms = timed(lambda: fa.attn_bf16_fwd(qb, kb, vb, causal=w.causal, out=(ob, lb)), n)
+            del qb, kb, vb
+            r.update({"bf16_ms": round(bf_ms, 4), "bf16_tflops": round(flops / (bf_ms * 1e-3) / 1e12, 2),
+                      "fp8_speedup_over_bf16": round(bf_ms / attn_ms, 3)})
+        quant()
+        attn()
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(11).choice(N, size=min(N, 512), replace=False))
+        heads = [(0, 0), (B - 1, H - 1)]
+        ridx = torch.from_numpy(rows).to(dev)
+        grab = lambda t: [t[b, h].index_select(0, ridx).float().cpu().numpy().astype(np.float64) for b, h in heads]
+        samples.append((name, w, arrs, rows, heads, grab(o), grab(ob) if ob is not None else None))
+        out[name] = r
+    cache.clear()
+    return out, samples
+
+
+def config_accuracy(configs, samples):
+    """Oracle leg, continued: RMSE and cosine against FP64 exact attention of the
+    FP8 path (and the BF16 twin) for each configuration, on the sampled rows."""
+    import numpy as np
+
+    from oracle import attention as oatt
+
+    for name, w, (q_np, k_np, v_np), rows, heads, o8, o16 in samples:
+        e8, e16, ra = [], [], []
+        for i, (b, h) in enumerate(heads):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            orf, _ = oatt.reference_attention(q_np[sl], k_np[sl], v_np[sl], w.causal, rows=rows)
+            e8.append((o8[i] - orf[0, 0]).ravel())
+            if o16 is not None:
+                e16.append((o16[i] - orf[0, 0]).ravel())
+            ra.append(orf[0, 0].ravel())
+        e8, ra = np.concatenate(e8), np.concatenate(ra)
+        cos = lambda e: float(np.dot(ra + e, ra) / (np.linalg.norm(ra + e) * np.linalg.norm(ra)))
+        acc = {"sample": f"{len(heads)} heads x {len(rows)} query rows vs FP64 exact attention",
+               "fp8_rmse": float(np.sqrt(np.mean(e8 ** 2))), "fp8_max_err": float(np.max(np.abs(e8))),
+               "fp8_cosine": cos(e8), "rms_o": float(np.sqrt(np.mean(ra ** 2)))}
+        if e16:
+            e16 = np.concatenate(e16)
+            acc.update({"bf16_rmse": float(np.sqrt(np.mean(e16 ** 2))), "bf16_cosine": cos(e16)})
+            acc["ratio_fp8_to_bf16_rmse"] = acc["fp8_rmse"] / acc["bf16_rmse"] if acc["bf16_rmse"] > 0 else None
+        configs[name]["accuracy"] = acc
 
 
 DECODE_NAMES = ("decode_gqa", "decode_gqa_spec")
