@@ -7,30 +7,56 @@
 // against ("FP8 attention that keeps FlashAttention-3 throughput at
 // BF16-level accuracy", What is asked).
 //
-// Same structure as the FP8 kernel: 4 waves x 32 queries, S^T = K Q^T so each
-// lane owns one query, P^T in registers as the B operand of O^T += V^T P^T,
-// V^T via ds_read_b64_tr_b16 from a row-major V tile, two-slot LDS ring fed
-// by direct global->LDS loads, lazy rescale.  Key tile: 64 keys (a 16 KB tile
-// at D = 128).
+// The loop has the FP8 kernel's structure, with 32-key tiles (one tile is
+// 32 x 2D bytes: 8 KiB at D = 128, the size of an FP8 64-key tile):
+//   * one workgroup = 4 waves x 32 queries of one head; S^T = K Q^T, so each
+//     lane of the accumulator owns one query and 16 keys (max and sum
+//     in-lane up to one exchange of the lane halves); Q resident in
+//     registers as the B operand;
+//   * P^T in BF16 is directly the B operand of O^T += V^T P^T; the V^T
+//     operand comes from the row-major V tile through ds_read_b64_tr_b16;
+//   * K and V stream through three-slot LDS rings, two tiles ahead, by
+//     buffer loads that write LDS (scalar addresses plus one per-lane offset;
+//     rows past the end read as zeros); each step waits only for the loads
+//     issued two steps earlier;
+//   * step t: phase A forms P_t (exponentials, row sum, BF16 pack) with the
+//     lazy reference max; a barrier; phase B adds V_t^T P_t^T to O and
+//     computes S_{t+1}.  P_t is formed against the current reference first,
+//     and the tile maximum is taken only when some lane's row sum shows that
+//     the reference may have to move (the decisions of taking it on every
+//     tile: the reference moves when a tile's largest scaled score exceeds
+//     it by more than kTauBf16);
+//   * an unrolled main loop over tiles that are complete and visible to every
+//     query of the workgroup (ring slots as constants, no masks), then the
+//     diagonal and ragged tiles in a tail with run-time slots.
 #include "common.h"
 #include "attn_internal.h"
 
 namespace attnfp8 {
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> two BF16 values (round to nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32 for the pair
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 constexpr float kTauBf16 = 8.0f;
+constexpr int kBf16Ring = 3;
+constexpr int kBf16KeyTile = 32;
 
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BC = 64;
-  static constexpr int KSTEPS = D / 16;      // 32x32x16 K-steps of QK^T
-  static constexpr int NSUB = BC / 32;
-  static constexpr int NKG = BC / 16;        // 16-key steps of PV
-  static constexpr int NDT = D / 32;
+  static constexpr int BC = kBf16KeyTile;    // keys per tile
+  static constexpr int KSTEPS = D / 16;      // 32x32x16 K-steps of S^T = K Q^T
+  static constexpr int NKG = BC / 16;        // 16-key steps of P V
+  static constexpr int NDT = D / 32;         // 32-row (d) tiles of O^T
   static constexpr int ROWB = 2 * D;         // bytes per row
-  static constexpr int SLOTS = ROWB / 16;
   static constexpr int TILE = BC * ROWB;
-  static constexpr int CHUNKS = TILE / 1024;
-  static constexpr int CHUNKS_PER_WAVE = CHUNKS / kWaves;
+  static constexpr int CHUNKS = TILE / 1024; // 1 KiB direct-load chunks per tile
+  static constexpr int CPW = CHUNKS / kWaves;
   static_assert(CHUNKS % kWaves == 0, "tile must split evenly over the waves");
 };
 
@@ -41,7 +67,8 @@ struct Bf16Cfg {
 //   K (ds_read_b128, 16 lanes per cycle, one row per lane): any 16 consecutive
 //     rows at one logical slot land in 16 distinct 16-byte bank groups.
 //   V (ds_read_b64_tr_b16, 32 lanes per cycle: 4 consecutive rows x 4 slots of
-//     one d-tile): the 4 rows' slot groups are disjoint.
+//     one d-tile): the 4 rows' slot groups are disjoint.  It depends on row % 4
+//     only.
 template <int D>
 __device__ __forceinline__ int swz_k16(int row) {
   if constexpr (D == 128) return row & 15;
@@ -53,158 +80,190 @@ __device__ __forceinline__ int swz_v16(int row) {
   else return 2 * (row & 3);
 }
 
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile16(const uint16_t* __restrict__ src, uint8_t* buf, int kt, int N,
-                                            int wave, int lane) {
+// Per-lane constants: LDS byte offsets (inside a tile) of the MFMA operands and
+// of the 16-byte pieces this lane moves in the tile loads.
+template <int D>
+struct Bf16Lane {
   using C = Bf16Cfg<D>;
-  const uint8_t* s8 = (const uint8_t*)src;
+  int k[C::KSTEPS];          // K row (lane % 32), slot 2 ks + h
+  int v[C::NDT];             // V^T source of d-tile dt at key step 0; + (16 kg + 8 rr) rows
+  int koff[C::CPW];          // tile-load source offsets (K, V swizzles)
+  int voff[C::CPW];
+  uint32_t lds0;             // LDS address of this wave's first chunk in slot 0
+
+  __device__ __forceinline__ Bf16Lane(int wave, int lane, uint32_t smem_addr) {
+    const int ql = lane & 31;
+    const int h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < C::CHUNKS_PER_WAVE; ++i) {
-    const int c = wave * C::CHUNKS_PER_WAVE + i;
-    const int pos = c * 1024 + lane * 16;
-    const int prow = pos / C::ROWB;
-    const int pslot = (pos % C::ROWB) / 16;
-    const int lslot = pslot ^ (IS_V ? swz_v16<D>(prow) : swz_k16<D>(prow));
-    int grow = kt * C::BC + prow;
-    grow = grow < N ? grow : N - 1;
-    global_to_lds16(s8 + (size_t)grow * C::ROWB + lslot * 16, buf + c * 1024);
+    for (int ks = 0; ks < C::KSTEPS; ++ks) k[ks] = ql * C::ROWB + 16 * ((2 * ks + h) ^ swz_k16<D>(ql));
+    // ds_read_b64_tr_b16: lane j of each 16-lane group receives element j % 4 of
+    // the rows named by lanes j / 4, j / 4 + 4, ...; source lane i of group g names
+    // key row 4 (g / 2) + i / 4 (+ 8 for the second read, + 16 per key step) and
+    // columns 32 dt + 16 (g % 2) + 4 (i % 4) .. + 3.  The other rows differ by
+    // multiples of 4, so the V swizzle of row0 holds for all of them.
+    const int g = lane >> 4;
+    const int i = lane & 15;
+    const int row0 = 4 * (g >> 1) + (i >> 2);
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const int slot = 4 * dt + 2 * (g & 1) + ((i & 3) >> 1);
+      v[dt] = row0 * C::ROWB + 16 * (slot ^ swz_v16<D>(row0)) + 8 * (i & 1);
+    }
+#pragma unroll
+    for (int c = 0; c < C::CPW; ++c) {
+      const int pos = (wave * C::CPW + c) * 1024 + lane * 16;
+      const int prow = pos / C::ROWB;
+      const int pslot = (pos % C::ROWB) / 16;
+      koff[c] = prow * C::ROWB + 16 * (pslot ^ swz_k16<D>(prow));
+      voff[c] = prow * C::ROWB + 16 * (pslot ^ swz_v16<D>(prow));
+    }
+    lds0 = smem_addr + wave * C::CPW * 1024;
+  }
+};
+
+// This wave's share of key tile kt of one head into the LDS slot at byte offset
+// slot_off.  Bytes at or past lim_bytes read as zeros.
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_tile16(const uint8_t* head, uint32_t lim_bytes, int kt, uint32_t slot_off,
+                                             const Bf16Lane<D>& ln) {
+  using C = Bf16Cfg<D>;
+  // (64-bit: the prefetches run up to three tiles past the end of a head whose
+  // size may come close to 2^31 bytes)
+  const long long off = (long long)kt * C::TILE;
+  const long long rem = (long long)lim_bytes - off;
+  const v4i rsrc = make_rsrc(head + off, (uint32_t)(rem > 0 ? rem : 0));
+#pragma unroll
+  for (int c = 0; c < C::CPW; ++c)
+    buffer_to_lds16(rsrc, IS_V ? ln.voff[c] : ln.koff[c], ln.lds0 + slot_off + c * 1024);
+}
+
+template <int D>
+struct Bf16State {
+  v16f o[Bf16Cfg<D>::NDT];
+  float m_ref;                // reference max (log2 units)
+  float l_acc;                // this lane's half of the row sum
+  v4i pop[Bf16Cfg<D>::NKG];   // P^T of the last tile in BF16
+};
+
+// S^T of a tile: 32 keys x 32 queries
+template <int D>
+__device__ __forceinline__ v16f qk16(const uint8_t* kbuf, const Bf16Lane<D>& ln,
+                                     const v4i (&qop)[Bf16Cfg<D>::KSTEPS]) {
+  v16f acc = {};
+#pragma unroll
+  for (int ks = 0; ks < Bf16Cfg<D>::KSTEPS; ++ks) acc = mfma_bf16(lds_read_b128(kbuf + ln.k[ks]), qop[ks], acc);
+  return acc;
+}
+
+// keys past the sequence, and (causal) past each query's position -> -inf
+template <bool CAUSAL>
+__device__ __forceinline__ void mask16(v16f& s, int t, int N, int lane, int iw, int my_q) {
+  const int k0 = t * kBf16KeyTile;
+  if ((k0 + kBf16KeyTile > N) || (CAUSAL && k0 + kBf16KeyTile - 1 > iw)) {
+    const int lim = (CAUSAL ? (my_q < N - 1 ? my_q : N - 1) : N - 1) - k0 - 4 * (lane >> 5);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) > lim) s[r] = -INFINITY;
+  }
+}
+
+// P = 2^(s c - m) in BF16 into pop (key step kg: accumulator entries
+// r = 8 kg .. 8 kg + 7); returns this lane's share of the row sum
+template <int D>
+__device__ __forceinline__ float p16(const v16f& s, Bf16State<D>& st, float c) {
+  const float b = -st.m_ref;
+  float rs = 0.0f;
+#pragma unroll
+  for (int kg = 0; kg < Bf16Cfg<D>::NKG; ++kg)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int r = 8 * kg + 2 * a;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, b));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, b));
+      rs += p0 + p1;
+      st.pop[kg][a] = (int)pk_bf16(p0, p1);
+    }
+  return rs;
+}
+
+// Phase A of a step: P of the tile in s, with the lazy reference update
+template <int D>
+__device__ __forceinline__ void bf16_phaseA(const v16f& s, Bf16State<D>& st, float c) {
+  float alpha = 1.0f;
+  float rs = p16<D>(s, st, c);
+  // every P is at most the row sum: while no lane's sum reaches 2^tau (less a
+  // margin for the rounding of the exponent argument), no P exceeds it and the
+  // reference stays (written so that a NaN sum counts as reaching it)
+  if (__builtin_amdgcn_ballot_w64(!(rs <= 256.0f * (1.0f - 1.0f / 64.0f)))) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    float tmax = mx * c;            // c > 0: the max commutes with the scale
+    tmax = fmaxf(tmax, swap_halves(tmax));
+    const bool upd = tmax > st.m_ref + kTauBf16;
+    if (__builtin_amdgcn_ballot_w64(upd)) {
+      const float m_new = upd ? tmax : st.m_ref;
+      alpha = upd ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
+      st.m_ref = m_new;
+#pragma unroll
+      for (int dt = 0; dt < Bf16Cfg<D>::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[dt][r] *= alpha;
+      rs = p16<D>(s, st, c);
+    }
+  }
+  st.l_acc = alpha * st.l_acc + rs;
+}
+
+// Phase B: O^T += V_t^T P_t^T, then S_{t+1} (when the wave computes it)
+template <int D, bool CAUSAL, bool MASK_NEXT>
+__device__ __forceinline__ void bf16_phaseB(v16f& s, const uint8_t* vcur, const uint8_t* knext, const Bf16Lane<D>& ln,
+                                            const v4i (&qop)[Bf16Cfg<D>::KSTEPS], Bf16State<D>& st, int t, int N,
+                                            int lane, int iw, int my_q, bool pv_active, bool next_valid) {
+  using C = Bf16Cfg<D>;
+  if (!MASK_NEXT || pv_active) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int kg = 0; kg < C::NKG; ++kg) {
+        const v2i lo = lds_read_tr16(vcur + (16 * kg) * C::ROWB + ln.v[dt]);
+        const v2i hi = lds_read_tr16(vcur + (16 * kg + 8) * C::ROWB + ln.v[dt]);
+        const v4i a = {lo[0], lo[1], hi[0], hi[1]};
+        st.o[dt] = mfma_bf16(a, st.pop[kg], st.o[dt]);
+      }
+  }
+  // (a tile this wave will not visit must not move the reference max)
+  if (!MASK_NEXT || next_valid) {
+    s = qk16<D>(knext, ln, qop);
+    if (MASK_NEXT) mask16<CAUSAL>(s, t + 1, N, lane, iw, my_q);
   }
 }
 
 template <int D, bool CAUSAL>
-struct Bf16Tile {
+__global__ __launch_bounds__(256, 3) void attn_bf16_kernel(AttnBf16Params p) {
   using C = Bf16Cfg<D>;
-
-  static __device__ __forceinline__ void run(const uint8_t* kbuf, const uint8_t* vbuf, int kt, int N, int lane,
-                                             int iw, int my_q, const v4i (&qop)[C::KSTEPS], float c,
-                                             v16f (&o)[C::NDT], float& m_ref, float& l_acc) {
-    const int ql = lane & 31;
-    const int h = lane >> 5;
-
-    v16f s[C::NSUB];
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      const int row = sub * 32 + ql;
-      const uint8_t* rp = kbuf + row * C::ROWB;
-      const int sw = swz_k16<D>(row);
-      v16f acc = {};
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        v4i a = lds_read_b128(rp + 16 * ((2 * ks + h) ^ sw));
-        acc = mfma_bf16(a, qop[ks], acc);
-      }
-      s[sub] = acc;
-    }
-
-    const int k0 = kt * C::BC;
-    const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > iw);
-    if (need_mask) {
-      const int lim = CAUSAL ? (my_q < N - 1 ? my_q : N - 1) : N - 1;
-#pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > lim) s[sub][r] = -INFINITY;
-        }
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    float tmax = mx * c;
-    tmax = fmaxf(tmax, swap_halves(tmax));
-    const bool upd = tmax > m_ref + kTauBf16;
-    const float m_new = upd ? tmax : m_ref;
-    const float alpha = upd ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-    m_ref = m_new;
-
-    // P (bf16) as the B operand: per 16-key step, 8 keys per lane
-    const float bias = -m_ref;
-    float rs = 0.0f;
-    v4i pop[C::NKG];
-#pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub)
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int r = 8 * kg + 2 * a;
-          float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][r], c, bias));
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][r + 1], c, bias));
-          rs += p0 + p1;
-          pop[2 * sub + kg][a] = (int)pack_bf16x2(p0, p1);
-        }
-    l_acc = alpha * l_acc + rs;
-
-    if (__builtin_amdgcn_ballot_w64(upd)) {
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-
-    // V^T operand: lane (d = l%32, half gh) needs V[key(j)][d] for j = 0..7 of each
-    // 16-key step; two ds_read_b64_tr_b16, source lane i supplies key j = 4*rr + i/4
-    // at columns d0 + 4*(i%4) .. +3.
-    const int g = lane >> 4;
-    const int i = lane & 15;
-    const int gh = g >> 1;
-    const int gd = g & 1;
-#pragma unroll
-    for (int kg = 0; kg < C::NKG; ++kg) {
-      int rows[2];
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int j = 4 * rr + (i >> 2);
-        rows[rr] = 16 * kg + 8 * (j >> 2) + 4 * gh + (j & 3);
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const int col = 32 * dt + 16 * gd + 4 * (i & 3);   // first element
-        const int slot = col / 8;                          // 16-byte column
-        const int within = (col % 8) * 2;                  // byte offset inside it
-        v2i part[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int row = rows[rr];
-          part[rr] = lds_read_tr16(vbuf + row * C::ROWB + 16 * (slot ^ swz_v16<D>(row)) + within);
-        }
-        v4i a = {part[0][0], part[0][1], part[1][0], part[1][1]};
-        o[dt] = mfma_bf16(a, pop[kg], o[dt]);
-      }
-    }
-  }
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnBf16Params p) {
-  using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kBf16Ring * C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N;
 
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / p.n_qtiles;
-  int qt = logical % p.n_qtiles;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;
+  // (uniform results of a division on the vector ALU: back to scalar registers)
+  const int bh = __builtin_amdgcn_readfirstlane(logical / p.n_qtiles);
+  int qt = __builtin_amdgcn_readfirstlane(logical - bh * p.n_qtiles);
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;            // longest tiles first
   const int i0 = qt * kQueryTile;
   const int iw = i0 + wave * kQueriesPerWave;
   const int my_q = iw + (lane & 31);
   const int h = lane >> 5;
 
   const size_t head = (size_t)bh * N * D;
-  const uint16_t* __restrict__ kh = p.k + head;
-  const uint16_t* __restrict__ vh = p.v + head;
+  const uint8_t* kh = (const uint8_t*)(p.k + head);
+  const uint8_t* vh = (const uint8_t*)(p.v + head);
 
+  // queries of this lane as the B operand: Q[q][16 ks + 8 h .. + 7]
   v4i qop[C::KSTEPS];
   {
     const int qrow = my_q < N ? my_q : N - 1;
@@ -214,45 +273,89 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnBf16Params p) {
   }
 
   const int n_kt = (N + C::BC - 1) / C::BC;
-  int n_kt_wg = n_kt;
-  int kt_w = n_kt - 1;
+  int n_kt_wg = n_kt;              // key tiles the workgroup steps through
+  int kt_w = n_kt - 1;             // last key tile this wave computes
+  int n_clean = N / C::BC;         // leading tiles complete and visible to every query here
   if (CAUSAL) {
     const int last_wg = (i0 + kQueryTile - 1 < N - 1) ? i0 + kQueryTile - 1 : N - 1;
     n_kt_wg = last_wg / C::BC + 1;
     const int last_w = (iw + kQueriesPerWave - 1 < N - 1) ? iw + kQueriesPerWave - 1 : N - 1;
     kt_w = last_w / C::BC;
+    n_clean = n_clean < i0 / C::BC ? n_clean : i0 / C::BC;
   }
+  // bytes of K / V this workgroup reads; loads past them return zeros
+  const int rows_wg = N < n_kt_wg * C::BC ? N : n_kt_wg * C::BC;
+  const uint32_t lim = (uint32_t)rows_wg * C::ROWB;
 
-  v16f o[C::NDT];
+  const Bf16Lane<D> ln(wave, lane, lds_addr_of(smem));
+  Bf16State<D> st;
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = (v16f){};
-  float m_ref = -1e30f;
-  float l_acc = 0.0f;
+  for (int dt = 0; dt < C::NDT; ++dt) st.o[dt] = (v16f){};
+  st.m_ref = -1e30f;
+  st.l_acc = 0.0f;
+#pragma unroll
+  for (int kg = 0; kg < C::NKG; ++kg) st.pop[kg] = (v4i){};
+  const float c = p.score_scale;
+  constexpr uint32_t KS = 0, VS = kBf16Ring * C::TILE;   // ring bases (byte offsets in smem)
 
-  load_tile16<D, false>(kh, kbuf0, 0, N, wave, lane);
-  load_tile16<D, true>(vh, vbuf0, 0, N, wave, lane);
+  // prologue: K0, K1, K2, V0, V1 resident; S_0 (masked)
+  issue_tile16<D, false>(kh, lim, 0, KS + 0 * C::TILE, ln);
+  issue_tile16<D, false>(kh, lim, 1, KS + 1 * C::TILE, ln);
+  issue_tile16<D, false>(kh, lim, 2, KS + 2 * C::TILE, ln);
+  issue_tile16<D, true>(vh, lim, 0, VS + 0 * C::TILE, ln);
+  issue_tile16<D, true>(vh, lim, 1, VS + 1 * C::TILE, ln);
+  wait_vmem_all();
+  __syncthreads();
+  v16f s = qk16<D>(smem + KS, ln, qop);
+  mask16<CAUSAL>(s, 0, N, lane, iw, my_q);
 
-  for (int kt = 0; kt < n_kt_wg; kt += 2) {
-    wait_vmem_all();
-    __syncthreads();
-    if (kt + 1 < n_kt_wg) {
-      load_tile16<D, false>(kh, kbuf1, kt + 1, N, wave, lane);
-      load_tile16<D, true>(vh, vbuf1, kt + 1, N, wave, lane);
-    }
-    if (kt <= kt_w)
-      Bf16Tile<D, CAUSAL>::run(kbuf0, vbuf0, kt, N, lane, iw, my_q, qop, p.score_scale, o, m_ref, l_acc);
-    if (kt + 1 >= n_kt_wg) break;
-    wait_vmem_all();
-    __syncthreads();
-    if (kt + 2 < n_kt_wg) {
-      load_tile16<D, false>(kh, kbuf0, kt + 2, N, wave, lane);
-      load_tile16<D, true>(vh, vbuf0, kt + 2, N, wave, lane);
-    }
-    if (kt + 1 <= kt_w)
-      Bf16Tile<D, CAUSAL>::run(kbuf1, vbuf1, kt + 1, N, lane, iw, my_q, qop, p.score_scale, o, m_ref, l_acc);
+  // Step t: phase A (P_t), then wait until only the previous step's loads are
+  // outstanding and barrier: K_{t+1} and V_t (issued two steps earlier) are
+  // resident for every wave, and every wave has finished reading K_t and
+  // V_{t-1}.  The step issues K_{t+3} (into K_t's slot) and V_{t+2} (into
+  // V_{t-1}'s slot), then runs phase B.  Tile j lives in ring slot j % 3.
+  const int t_main = n_clean - 1;
+  int t = 0;
+#define BF16_STEP(I, KN, KF, VC, VF)                                                                        \
+  {                                                                                                       \
+    const int tt = t + (I);                                                                               \
+    if (tt >= t_main) {                                                                                   \
+      t = tt;                                                                                             \
+      break;                                                                                              \
+    }                                                                                                     \
+    bf16_phaseA<D>(s, st, c);                                                                             \
+    wait_vmem_prev_step<2 * C::CPW>();                                                                    \
+    workgroup_barrier();                                                                                  \
+    issue_tile16<D, false>(kh, lim, tt + 3, KS + (KF) * C::TILE, ln);                                    \
+    issue_tile16<D, true>(vh, lim, tt + 2, VS + (VF) * C::TILE, ln);                                     \
+    bf16_phaseB<D, CAUSAL, false>(s, smem + VS + (VC) * C::TILE, smem + KS + (KN) * C::TILE, ln, qop, st, tt, N, \
+                                  lane, iw, my_q, true, true);                                            \
   }
+  for (;; t += 3) {
+    BF16_STEP(0, 1, 0, 0, 2)
+    BF16_STEP(1, 2, 1, 1, 0)
+    BF16_STEP(2, 0, 2, 2, 1)
+  }
+#undef BF16_STEP
 
-  const float l_tot = l_acc + swap_halves(l_acc);
+  // Tail: diagonal and ragged tiles, waves that stop early; run-time slots and
+  // full waits (vmcnt(0)), which stay correct whatever other memory operations
+  // the compiler schedules here.
+  for (; t < n_kt_wg; ++t) {
+    const bool active = t <= kt_w;
+    if (active) bf16_phaseA<D>(s, st, c);
+    wait_vmem_all();
+    workgroup_barrier();
+    issue_tile16<D, false>(kh, lim, t + 3, KS + (t % kBf16Ring) * C::TILE, ln);
+    issue_tile16<D, true>(vh, lim, t + 2, VS + ((t + 2) % kBf16Ring) * C::TILE, ln);
+    bf16_phaseB<D, CAUSAL, true>(s, smem + VS + (t % kBf16Ring) * C::TILE,
+                                 smem + KS + ((t + 1) % kBf16Ring) * C::TILE, ln, qop, st, t, N, lane, iw, my_q,
+                                 active, t + 1 <= kt_w);
+  }
+  wait_vmem_all();   // no tile load may still be writing LDS when the workgroup ends
+
+  // ---- epilogue: O = O_acc / l ; LSE = ln 2 * (m + log2 l)
+  const float l_tot = st.l_acc + swap_halves(st.l_acc);
   const float inv_l = 1.0f / l_tot;
   if (my_q < N) {
     uint16_t* orow = p.o + head + (size_t)my_q * D;
@@ -261,11 +364,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnBf16Params p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d = 32 * dt + 8 * a + 4 * h;
-        uint32_t w0 = pack_bf16x2(o[dt][4 * a + 0] * inv_l, o[dt][4 * a + 1] * inv_l);
-        uint32_t w1 = pack_bf16x2(o[dt][4 * a + 2] * inv_l, o[dt][4 * a + 3] * inv_l);
+        uint32_t w0 = pk_bf16(st.o[dt][4 * a + 0] * inv_l, st.o[dt][4 * a + 1] * inv_l);
+        uint32_t w1 = pk_bf16(st.o[dt][4 * a + 2] * inv_l, st.o[dt][4 * a + 3] * inv_l);
         *(v2i*)(orow + d) = (v2i){(int)w0, (int)w1};
       }
-    if (h == 0) p.lse[(size_t)bh * N + my_q] = kLn2 * (m_ref + __builtin_amdgcn_logf(l_tot));
+    if (h == 0) p.lse[(size_t)bh * N + my_q] = kLn2 * (st.m_ref + __builtin_amdgcn_logf(l_tot));
   }
 }
 

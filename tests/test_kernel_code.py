@@ -21,6 +21,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "fp8_attention_forward_amd", "csrc", "attn_fp8.hip")
 DECODE_SRC = os.path.join(ROOT, "fp8_attention_forward_amd", "csrc", "attn_decode.hip")
+BF16_SRC = os.path.join(ROOT, "fp8_attention_forward_amd", "csrc", "attn_bf16.hip")
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
 
 pytestmark = pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
@@ -88,8 +89,23 @@ def _code(lines):
     return [l.strip() for l in lines if l.strip() and not l.strip().startswith(";")]
 
 
-def test_every_lds_dma_carries_its_wait_states(kernels, decode_kernels):
-    for name, lines in list(kernels.items()) + list(decode_kernels.items()):
+@pytest.fixture(scope="module")
+def bf16_kernels():
+    funcs = _compile(BF16_SRC, "16attn_bf16_kernel")
+    assert len(funcs) == 4, sorted(funcs)   # D x causal
+    return funcs
+
+
+def test_bf16_kernels_run_three_waves_per_simd(bf16_kernels):
+    # 48 KiB of LDS per workgroup at D = 128 (two three-slot rings of 8 KiB
+    # tiles): three workgroups per CU, so three waves per SIMD must fit the
+    # registers too
+    for name, (scratch, occ) in _resources(BF16_SRC, bf16_kernels).items():
+        assert occ >= 3, f"{name}: {occ} waves per SIMD"
+
+
+def test_every_lds_dma_carries_its_wait_states(kernels, decode_kernels, bf16_kernels):
+    for name, lines in list(kernels.items()) + list(decode_kernels.items()) + list(bf16_kernels.items()):
         code = _code(lines)
         n = 0
         for i, ins in enumerate(code):
@@ -135,11 +151,11 @@ def _asm_blocks(lines):
     return out
 
 
-def test_partial_tile_waits_count_only_tile_loads(kernels):
+def test_partial_tile_waits_count_only_tile_loads(kernels, bf16_kernels):
     """A loop that waits for its tile loads with a partial vmcnt (the kernel's
     own inline s_waitcnt) must not contain vector-memory operations of the
     compiler's own, which that count does not include."""
-    for name, lines in kernels.items():
+    for name, lines in list(kernels.items()) + list(bf16_kernels.items()):
         n_partial = 0
         for lab, body in _loops(lines):
             mine = [w for w in _asm_blocks(body) if re.match(r"s_waitcnt vmcnt\((\d+)\)", w)]
