@@ -339,8 +339,9 @@ __global__ __launch_bounds__(256, 3) void attn_bf16_kernel(AttnBf16Params p) {
 #undef BF16_STEP
 
   // Tail: diagonal and ragged tiles, waves that stop early; run-time slots and
-  // full waits (vmcnt(0)), which stay correct whatever other memory operations
-  // the compiler schedules here.
+  // full waits (vmcnt(0)): at D = 128 the causal instance reloads a spilled
+  // register in this loop, a vector-memory operation that a partial count of
+  // the tile loads would not include.
   for (; t < n_kt_wg; ++t) {
     const bool active = t <= kt_w;
     if (active) bf16_phaseA<D>(s, st, c);
