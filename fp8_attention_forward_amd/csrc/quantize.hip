@@ -19,7 +19,8 @@
 // With power-of-two scales (the microscaling form, FLAMIA 2 Background) the
 // descale is the smallest 2^e that keeps the block's amax inside +-448.
 //
-// Memory: reads 4 B and writes 1 B per element (HBM bound).
+// Memory: reads 4 B and writes 1 B per element (HBM bound), both with
+// non-temporal accesses (each byte is touched once).
 #include "common.h"
 #include "attn_internal.h"
 
@@ -94,7 +95,9 @@ __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, i
   for (int it = 0; it < ITERS; ++it) {
     const int row = it * RPI + tid / LPR;
     if (row < nrows) {
-      v4f t = *(const v4f*)(src + (size_t)row * D + c0);
+      // (read once and never again: non-temporal, so the stream does not
+      // displace reusable lines from the caches)
+      v4f t = __builtin_nontemporal_load((const v4f*)(src + (size_t)row * D + c0));
       x[it][0] = t[0]; x[it][1] = t[1]; x[it][2] = t[2]; x[it][3] = t[3];
     } else {
       x[it][0] = x[it][1] = x[it][2] = x[it][3] = 0.0f;
@@ -158,7 +161,7 @@ __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, i
     for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(x[it][e] * inv, -448.0f), 448.0f);
     int packed = cvt_pk_fp8<false>(v[0], v[1], 0);
     packed = cvt_pk_fp8<true>(v[2], v[3], packed);
-    if (row < nrows) *(int*)(dst + (size_t)row * D + c0) = packed;
+    if (row < nrows) __builtin_nontemporal_store(packed, (int*)(dst + (size_t)row * D + c0));
   }
 }
 
