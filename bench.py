@@ -55,6 +55,22 @@ def parse():
     return ap.parse_args()
 
 
+def smi_clocks():
+    """Clock limits the device reports (amd-smi, a child process; None if unavailable).
+    The clock held under load is not sampled here: the rocprofv3 summaries derive
+    it from GRBM_GUI_ACTIVE over the launch time."""
+    import subprocess
+    try:
+        res = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True, text=True,
+                             timeout=30)
+        clk = json.loads(res.stdout)["gpu_data"][0]["clock"]
+        mhz = lambda d, key: d[key]["value"] if isinstance(d.get(key), dict) else None
+        return {"gfx_min_mhz": mhz(clk["gfx_0"], "min_clk"), "gfx_max_mhz": mhz(clk["gfx_0"], "max_clk"),
+                "mem_mhz": mhz(clk["mem_0"], "clk"), "source": "amd-smi metric --clock (device limits)"}
+    except Exception:
+        return None
+
+
 def kernel_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -302,7 +318,7 @@ def main():
         "toolchain": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                       "numpy": np.__version__, "hipcc": hipcc_version(),
                       "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
-                      "device": torch.cuda.get_device_name(0)},
+                      "device": torch.cuda.get_device_name(0), "clocks": smi_clocks()},
     }
 
     if not args.no_packed:
