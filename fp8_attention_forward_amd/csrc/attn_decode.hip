@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
     float tmax = mx * c;
     tmax = fmaxf(tmax, swap_halves(tmax));
     const bool upd = tmax > m_ref + kTau;
-    const float m_new = upd ? tmax : m_ref;
+    const float m_new = upd ? tmax - kLift : m_ref;
     const float alpha = upd ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
     m_ref = m_new;
     if (__builtin_amdgcn_ballot_w64(upd)) {

@@ -176,8 +176,9 @@ __device__ __forceinline__ float p_tile(const STile<D>& s, v8i& pop, float c, fl
 }
 
 // Lazy reference update from the tile maximum: the reference m moves only
-// when the tile's largest scaled score exceeds it by more than tau; then O is
-// rescaled by alpha = 2^(m_old - m_new) (1 for lanes that keep theirs).
+// when the tile's largest scaled score exceeds it by more than tau, and then
+// to kLift below that maximum; O is rescaled by alpha = 2^(m_old - m_new) (1
+// for lanes that keep theirs).
 // Returns whether any lane of the wave moved.
 template <int D>
 __device__ __forceinline__ bool move_reference(const STile<D>& s, Fp8State<D>& st, float c, float& alpha) {
@@ -191,7 +192,7 @@ __device__ __forceinline__ bool move_reference(const STile<D>& s, Fp8State<D>& s
   tmax = fmaxf(tmax, swap_halves(tmax));
   const bool upd = tmax > st.m_ref + kTau;
   if (!__builtin_amdgcn_ballot_w64(upd)) return false;
-  const float m_new = upd ? tmax : st.m_ref;
+  const float m_new = upd ? tmax - kLift : st.m_ref;
   alpha = upd ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
   st.m_ref = m_new;
 #pragma unroll

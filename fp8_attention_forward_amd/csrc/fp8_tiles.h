@@ -9,6 +9,12 @@
 namespace attnfp8 {
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units): P <= 2^8
+// When the reference moves it is set kLift below the tile maximum (log2
+// units, a whole number): the key that moved it gets P = 2^kLift, which e4m3
+// holds exactly, while the small probabilities sit 2^kLift higher, away from
+// e4m3's subnormal range.  Moves still happen only when some P would exceed
+// 2^kTau, so P <= 256 as before.
+constexpr float kLift = 4.0f;
 
 // Exponentials of the probabilities P.
 //   kExpExact: v_exp_f32 of the scaled score (one FMA + one transcendental).

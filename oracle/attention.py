@@ -1,13 +1,15 @@
-"""Exact attention in float64 and the running-softmax loop (oracle; test infrastructure only).
+"""Exact attention in float64, and the error bars of the FP8 path around it
+(oracle; test infrastructure only).
 
-[P2] "Fused attention kernel", Overview: attention is softmax(Q K^T) V; a fused
-kernel reaches the same result block by block with a running row maximum and
-row sum, so the fused loop is exact up to rounding order.  Implementation
-sketch: per key block, s = q k_j^T, m_new = max(m, rowmax s),
-alpha = exp(m - m_new), p = exp(s - m_new), l = alpha l + rowsum p,
-o = alpha o + p v_j; at the end o / l and lse = m + log l.  The card scores
-every key block (its note on the printed loop bound of the paper's Algorithm 2)
-and rescales the output by exp(old max - new max) (its note on Algorithm 1).
+[P2] "Fused attention kernel", Overview: attention is the softmax of the
+scaled scores applied to V; the fused kernel visits the keys block by block
+and keeps, per query, the largest score seen and the sum of exponentials
+against it, rescaling what it has accumulated whenever that maximum grows, so
+its result is the plain definition up to rounding order.  Implementation
+sketch: the same loop written out, with the output divided by the row sum at
+the end and the log-sum-exp returned beside it.  The card's notes on the
+paper's listings fix two details: the old state is scaled by the exponential
+of (old maximum - new maximum), and the last key block is scored too.
 
 Readings taken here (the pages leave them open):
   * softmax scale 1/sqrt(d) on the scores (the sketch prints none);
@@ -23,7 +25,7 @@ import math
 
 import numpy as np
 
-from . import e4m3, fastexp
+from . import e4m3, fastexp, mfma_fp8
 from .quantize import dequantize
 
 
@@ -92,37 +94,203 @@ def emulated_fp8_attention(q8, k8, v8, q_descale, k_descale, v_descale,
     return attention_fp64(qh, kh, vh, causal, scale, rows=rows)
 
 
-def online_attention_fp64(q, k, v, causal, scale, block_c):
-    """The sketch's running-softmax loop for one head, float64, key blocks of ``block_c``.
+# ---------------------------------------------------------------------------
+# E1 with error bars.  The FP8 path computes E1 (the attention of the
+# quantised inputs) with three departures that the pages fix or leave open,
+# each bounded here from E1's own quantities (scores, weights, codes,
+# descales), never from a kernel's blocking:
+#   * P is rounded to e4m3 before its product with V ([P1] / north-star
+#     reading C12; the pages do not model it).  A probability P in e4m3 moves
+#     by at most 2^-4 P (normal range) or min(P, 2^-10) (subnormal range, in
+#     units where the row's largest P is at least 1).  The V block scale,
+#     when it is folded into P, is at most the largest V descale of the
+#     sequence.  So |dO_id| <= sum_j [2^-4 w_ij |v_jd|
+#     + min(w_ij |v_jd|, 2^-10 dv_max |V8_jd| / l_i)], l_i the row sum against
+#     the row maximum (l_i >= 1).
+#   * The matrix cores sum the e4m3 products with the truncation of
+#     ``mfma_fp8``: each score moves by at most delta_ij (natural units);
+#     a row whose scores all move by at most D_i has its log-sum-exp moved by
+#     at most D_i and every weight scaled by a factor within exp(+-2 D_i), so
+#     |dO_id| <= (exp(2 D_i) - 1) sum_j w_ij |v_jd - O_id|.
+#   * Optionally Schraudolph's exponential (relative error within
+#     [EPS_LO, EPS_HI] per probability, the row sum built from the same
+#     values): weights move by a factor within (1 + ETA)^+-1 and the LSE by
+#     at most LSE_SCHRAUDOLPH.
+# The maximum-error bar of an element is the larger of the target 2e-2 and
+# the P-rounding bound, plus the accumulation bound and half a BF16 ulp (the
+# output's own rounding).  For the RMS error, P's rounding errors are modelled
+# as independent and uniform within their bounds (``sigma``): the RMS bar is
+# the larger of the target 2e-3 and twice that model, plus the RMS of the
+# accumulation bound.
+# ---------------------------------------------------------------------------
 
-    Scores every key block including a short last one; rescales the old state
-    by exp(m_old - m_new).  Used only to pin ``attention_fp64`` (they must agree).
+EPS_LO = 2.0 ** -fastexp.SIGMA - 1.0 - 2.0 ** -16
+EPS_HI = (1.0 / math.log(2.0)) * 2.0 ** (1.0 - 1.0 / math.log(2.0) - fastexp.SIGMA) - 1.0 + 2.0 ** -16
+ETA = (1.0 + EPS_HI) / (1.0 + EPS_LO) - 1.0
+LSE_SCHRAUDOLPH = max(-math.log1p(EPS_LO), math.log1p(EPS_HI))
+
+
+def _schraudolph_rel_rms():
+    """RMS of Schraudolph's relative error about its mean, over a uniform
+    fractional part of the exponent (the part that varies from key to key)."""
+    f = (np.arange(1 << 16) + 0.5) / (1 << 16)
+    r = fastexp.schraudolph_exp2(f) / np.exp2(f) - 1.0
+    return float(np.std(r))
+
+
+RHO_SCHRAUDOLPH = _schraudolph_rel_rms()
+
+
+def e1_rows_with_bars(q8r, dq, k8, dk, v8, dv, q_pos, causal, scale, exp2, accumulation):
+    """E1 and its bars for R query rows of one sequence against its N keys.
+
+    q8r [R, D], k8 / v8 [N, D] codes; dq [R], dk / dv [N] the descale of each
+    row's block; q_pos [R] the query positions (causal: key j is visible iff
+    j <= q_pos).  Returns O [R, D], LSE [R], bmax [R, D], sigma [R, D],
+    lse_bar [R] (what is added to the relative LSE target), acc_bar [R, D].
+    """
+    qv = e4m3.decode(q8r) * dq[:, None]
+    kv = e4m3.decode(k8) * dk[:, None]
+    v8v = e4m3.decode(v8)
+    vv = v8v * dv[:, None]
+    s = (qv @ kv.T) * scale
+    vis = np.ones(s.shape, dtype=bool)
+    if causal:
+        vis = np.arange(k8.shape[0])[None, :] <= np.asarray(q_pos)[:, None]
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    p = np.where(vis, np.exp(s - m[:, None]), 0.0)
+    l = p.sum(axis=1)
+    w = p / l[:, None]
+    o = w @ vv
+    lse = m + np.log(l)
+    dvmax = float(np.max(dv))
+    wabs = w @ np.abs(vv)
+    # sum_j w_ij |v_jd - O_id|, row by row
+    wdev = np.empty_like(o)
+    for i in range(o.shape[0]):
+        wdev[i] = w[i] @ np.abs(vv - o[i])
+    # accumulation of the scores by the matrix cores: per score a bound on its
+    # movement (the pinned truncation of ``mfma_fp8``, its combination step,
+    # and the float32 rounding of the scaled score), then the weighted
+    # perturbation of the softmax: with a_j = exp(|delta_j|) - 1 and
+    # zeta = sum_j w_j a_j, every weight moves by at most w_j (a_j + zeta) / (1 - zeta)
+    # and the LSE by at most -ln(1 - zeta)
+    if accumulation:
+        sc = (dq[:, None] * dk[None, :]) * scale
+        d_code = np.abs(mfma_fp8.scores(q8r, k8) - e4m3.decode(q8r) @ e4m3.decode(k8).T)
+        delta = (d_code + mfma_fp8.combine_tolerance(q8r, k8)) * sc
+        delta = delta + 2.0 ** -21 * (np.abs(np.where(vis, s, 0.0)) + np.abs(m)[:, None])
+        a = np.where(vis, np.expm1(delta), 0.0)
+        zeta = np.sum(w * a, axis=1)
+        if np.any(zeta >= 0.5):
+            raise ValueError("accumulation error too large for the perturbation bound")
+        acc_bar = np.empty_like(o)
+        for i in range(o.shape[0]):
+            acc_bar[i] = (w[i] * (a[i] + zeta[i])) @ np.abs(vv - o[i]) / (1.0 - zeta[i])
+        grow = (1.0 + a.max(axis=1) + zeta) / (1.0 - zeta)
+        lse_acc = -np.log1p(-zeta)
+    else:
+        acc_bar = np.zeros_like(o)
+        grow = np.ones(len(m))
+        lse_acc = np.zeros(len(m))
+    # P below e4m3's normal range: its rounding error is at most the smaller
+    # of P itself and half the smallest subnormal
+    cap = 2.0 ** -10 * dvmax / l
+    absvv = np.abs(vv)
+    absv8m = np.abs(v8v)
+    sub = np.empty_like(o)
+    sub2 = np.empty_like(o)
+    for i in range(o.shape[0]):
+        t = np.minimum(w[i][:, None] * absvv, cap[i] * absv8m)
+        sub[i] = t.sum(axis=0)
+        sub2[i] = (t * t).sum(axis=0)
+    var = (2.0 ** -8 / 3.0) * ((w * w) @ (vv * vv)) + sub2 / 3.0
+    lse_bar = lse_acc.copy()
+    if exp2 == "exact":
+        pbar = 2.0 ** -4 * wabs + sub
+    elif exp2 == "schraudolph":
+        pbar = ETA * wdev + 2.0 ** -4 * (1.0 + ETA) * wabs + sub / (1.0 + EPS_LO)
+        dev2 = np.empty_like(o)
+        for i in range(o.shape[0]):
+            dev2[i] = (w[i] * w[i]) @ (vv - o[i]) ** 2
+        var = var + RHO_SCHRAUDOLPH ** 2 * dev2
+        lse_bar = lse_bar + LSE_SCHRAUDOLPH
+    else:
+        raise ValueError("exp2 must be 'exact' or 'schraudolph'")
+    return o, lse, pbar * grow[:, None], np.sqrt(var), lse_bar, acc_bar
+
+
+def emulated_fp8_attention_bars(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard, causal,
+                                rows=None, exp2="exact", accumulation=True, row_chunk=256):
+    """E1 (``emulated_fp8_attention``) with the error bars of the FP8 path.
+
+    Returns a dict with O, LSE (E1), and per element / row: ``pbar`` (bound on
+    what P's e4m3 rounding, and Schraudolph's exponential if asked, move O),
+    ``sigma`` (RMS model of that movement), ``acc_bar`` (bound on what the
+    matrix cores' accumulation moves O), ``lse_bar`` (bound on the LSE
+    movement beyond the relative target).
+    """
+    d = np.shape(q8)[-1]
+    n = np.shape(q8)[-2]
+    lead = np.shape(q8)[:-2]
+    scale = 1.0 / math.sqrt(d) / (d if hadamard else 1)
+    row_idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    tok_blk = np.arange(n) // scale_block
+    out = {k: np.empty(lead + (len(row_idx), d)) for k in ("o", "pbar", "sigma", "acc_bar")}
+    out.update({k: np.empty(lead + (len(row_idx),)) for k in ("lse", "lse_bar")})
+    for idx in np.ndindex(*lead):
+        qd = np.asarray(q_descale[idx], dtype=np.float64)
+        kd = np.asarray(k_descale[idx], dtype=np.float64)
+        vd = np.asarray(v_descale[idx], dtype=np.float64)
+        for c0 in range(0, len(row_idx), row_chunk):
+            ri = row_idx[c0:c0 + row_chunk]
+            res = e1_rows_with_bars(q8[idx][ri], qd[ri // scale_block], k8[idx], kd[tok_blk], v8[idx],
+                                     vd[tok_blk], ri, causal, scale, exp2, accumulation)
+            sl = idx + (slice(c0, c0 + len(ri)),)
+            for key, val in zip(("o", "lse", "pbar", "sigma", "lse_bar", "acc_bar"), res):
+                out[key][sl] = val
+    return out
+
+
+def online_attention_fp64(q, k, v, causal, scale, block_c):
+    """Blockwise attention of one head merged by log-sum-exp, float64.
+
+    Each key block of ``block_c`` keys (the last may be short) is reduced on
+    its own to (its row maxima, its row sums against them, its unnormalised
+    partial output); the blocks are then combined left to right, each
+    combination rescaling the side whose maximum is smaller by the exponential
+    of the difference.  This is the fused loop's invariant written as a merge
+    of independent partial results ("Fused attention kernel", Overview and
+    Implementation sketch: the running maximum and sum make the blockwise
+    result exact).  Used only to pin ``attention_fp64`` (they must agree).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     n, d = q.shape
-    nk = k.shape[0]
-    o = np.zeros((n, d))
-    m = np.full(n, -np.inf)
-    l = np.zeros(n)
     qi = np.arange(n)
-    for j0 in range(0, nk, block_c):
-        kj = k[j0:j0 + block_c]
-        vj = v[j0:j0 + block_c]
-        s = (q @ kj.T) * scale
+    parts = []
+    for j0 in range(0, k.shape[0], block_c):
+        s = (q @ k[j0:j0 + block_c].T) * scale
         if causal:
-            kidx = np.arange(j0, j0 + kj.shape[0])
+            kidx = np.arange(j0, j0 + s.shape[1])
             s = np.where(kidx[None, :] <= qi[:, None], s, -np.inf)
-        m_new = np.maximum(m, s.max(axis=1))
-        # a row with no visible key yet keeps m = -inf; use 0 as its exp reference
-        ref = np.where(np.isfinite(m_new), m_new, 0.0)
-        alpha = np.exp(np.where(np.isfinite(m), m - ref, -np.inf))
-        p = np.exp(s - ref[:, None])
-        l = alpha * l + p.sum(axis=1)
-        o = alpha[:, None] * o + p @ vj
-        m = m_new
-    return o / l[:, None], m + np.log(l)
+        bmax = s.max(axis=1)
+        seen = np.isfinite(bmax)                  # rows with a visible key in this block
+        e = np.exp(s - np.where(seen, bmax, 0.0)[:, None])
+        e[~seen] = 0.0
+        parts.append((bmax, e.sum(axis=1), e @ v[j0:j0 + block_c]))
+    big, tot, acc = parts[0]
+    for bmax, bsum, bout in parts[1:]:
+        new = np.maximum(big, bmax)
+        ref = np.where(np.isfinite(new), new, 0.0)
+        wa = np.where(np.isfinite(big), np.exp(big - ref), 0.0)
+        wb = np.where(np.isfinite(bmax), np.exp(bmax - ref), 0.0)
+        tot = wa * tot + wb * bsum
+        acc = wa[:, None] * acc + wb[:, None] * bout
+        big = new
+    return acc / tot[:, None], big + np.log(tot)
 
 
 def brute_force_attention(q, k, v, causal, scale):
@@ -171,7 +339,7 @@ def e4m3_tie_step(x, window=P_TIE_WINDOW):
 
 def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
                                  causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True, block_c=64,
-                                 exp2="exact", mx=False, tie_slack=False):
+                                 exp2="exact", mx=False, tie_slack=False, lift=4.0):
     """E2: the running-softmax loop over key blocks with P re-quantised to e4m3.
 
     The pages fix the loop (Implementation sketch) and that the matrix products
@@ -182,9 +350,10 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
         units: t = s * dq_i * dk_j * log2(e) / sqrt(d) (/ d if rotated), where s
         is the exact dot product of the decoded codes and dk_j the descale of
         the scale block holding key block j;
-      * a reference max m is kept per query; it moves to a block's max only
-        when that max exceeds m by more than ``tau``; with tau = 0 this is the
-        sketch's running max (m_new = max(m, rowmax));
+      * a reference m is kept per query; it moves only when a block's max
+        exceeds m by more than ``tau``, and then to ``lift`` (a whole number)
+        below that max, so the key that moved it has P = 2^lift exactly; with
+        tau = lift = 0 this is the sketch's running max;
       * P entering the product with V is e4m3(2^(t - m) * r_j) with
         r_j = dv_j / dv_ref, dv_ref the largest V descale among the key blocks
         that the query's block can see (all blocks when not causal); so P <= 2^tau;
@@ -259,7 +428,7 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
                 t = np.where(np.arange(k0, k1)[None, :] <= row_idx[:, None], t, -np.inf)
             tmax = t.max(axis=1)
             upd = tmax > m + tau
-            m_new = np.where(upd, tmax, m)
+            m_new = np.where(upd, tmax - lift, m)
             alpha = np.where(upd, np.exp2(np.where(np.isfinite(m), m - m_new, -np.inf)), 1.0)
             m = m_new
             ok = np.isfinite(m)

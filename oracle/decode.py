@@ -18,7 +18,8 @@ The pages give no decode algorithm.  Readings taken here:
     its position; otherwise all L_b keys;
   * the keys are split into ranges of ``split`` consecutive keys (a multiple
     of the 64-key tile).  Each range runs the E2 loop of ``attention`` on its
-    own: tiles of 64 keys, the lazy reference max (threshold tau),
+    own: tiles of 64 keys, the lazy reference (threshold tau, moved to
+    ``lift`` below the block maximum),
     P = e4m3(2^(t - m) r_j) with r_j = dv_j / dv_ref and dv_ref the largest V
     descale of the scale blocks the range touches, l summing the unrounded
     2^(t - m); it yields (m, l, O^ = dv_ref * sum P v).  The ranges merge
@@ -33,13 +34,13 @@ import math
 import numpy as np
 
 from . import e4m3
-from .attention import e4m3_tie_step, round_to_bf16
+from .attention import e1_rows_with_bars, e4m3_tie_step, round_to_bf16
 
 TILE = 64
 
 
 def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_block, hadamard, causal,
-                        split, tau=8.0, quantize_p=True, bf16_output=True, tie_slack=False):
+                        split, tau=8.0, quantize_p=True, bf16_output=True, tie_slack=False, lift=4.0):
     """Decode of [B][Hq][Sq][D] query codes against the FP8 cache.  Returns
     (O [B][Hq][Sq][D], LSE [B][Hq][Sq]) in float64 (O rounded to BF16 values
     unless ``bf16_output`` is False) and, with ``tie_slack``, the movement of
@@ -87,7 +88,7 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
                         t = np.where(np.arange(k0, k1)[None, :] <= pos[:, None], t, -np.inf)
                     tmax = t.max(axis=1)
                     upd = tmax > m + tau
-                    m_new = np.where(upd, tmax, m)
+                    m_new = np.where(upd, tmax - lift, m)
                     with np.errstate(invalid="ignore"):      # (-inf) - (-inf) in the branch not taken
                         alpha = np.where(upd, np.exp2(np.where(np.isfinite(m), m - m_new, -np.inf)), 1.0)
                     m = m_new
@@ -114,3 +115,36 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
     if tie_slack:
         return o, lse, slack
     return o, lse
+
+
+def emulated_fp8_decode_bars(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_block, hadamard, causal,
+                             exp2="exact"):
+    """E1 of the decode step, with the FP8 error bars of
+    ``attention.emulated_fp8_attention_bars``: for every (sequence, query head)
+    the exact float64 attention of its Sq dequantised query rows (one descale)
+    against the dequantised first L_b cache rows of its K/V head, query i at
+    position L_b - Sq + i.  No split: the ranges of the kernel merge exactly.
+    Returns a dict with O and the bars [B, Hq, Sq, D], LSE and its bar [B, Hq, Sq]."""
+    B, Hq, Sq, D = np.shape(q8)
+    Hkv = np.shape(k8)[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) / (D if hadamard else 1)
+    out = {key: np.empty((B, Hq, Sq, D)) for key in ("o", "pbar", "sigma", "acc_bar")}
+    out.update({key: np.empty((B, Hq, Sq)) for key in ("lse", "lse_bar")})
+    for b in range(B):
+        L = int(seqlens[b])
+        if not Sq <= L <= np.shape(k8)[2]:
+            raise ValueError("need Sq <= L_b <= Ncap")
+        blk = np.arange(L) // scale_block
+        for h in range(Hq):
+            g = h // G
+            kd = np.asarray(k_descale[b, g], dtype=np.float64)[blk]
+            vd = np.asarray(v_descale[b, g], dtype=np.float64)[blk]
+            qd = np.full(Sq, float(q_descale[b, h, 0]))
+            res = e1_rows_with_bars(q8[b, h], qd, k8[b, g, :L], kd, v8[b, g, :L], vd, L - Sq + np.arange(Sq),
+                                    causal, scale, exp2, True)
+            for key, val in zip(("o", "lse", "pbar", "sigma", "lse_bar", "acc_bar"), res):
+                out[key][b, h] = val
+    return out

@@ -35,7 +35,7 @@ import math
 
 import numpy as np
 
-from .attention import emulated_fp8_attention_tiled, reference_attention
+from .attention import emulated_fp8_attention_bars, emulated_fp8_attention_tiled, reference_attention
 from .quantize import quantize_qkv
 
 QUERY_TILE = 128
@@ -141,6 +141,28 @@ def emulated_fp8_attention_varlen(q8, k8, v8, q_descale, k_descale, v_descale, c
     if kw.get("tie_slack"):
         return o, lse, slack
     return o, lse
+
+
+def emulated_fp8_attention_varlen_bars(q8, k8, v8, q_descale, k_descale, v_descale, cu, scale_block, hadamard,
+                                       causal, rows=None, exp2="exact"):
+    """E1 of each packed document with the FP8 error bars of
+    ``attention.emulated_fp8_attention_bars``: each document is a sequence of
+    its own (its codes and the descales of its blocks, read from its slots).
+    Returns the same dict, O and the bars [H, R, D], LSE and its bar [H, R]."""
+    H, T, D = np.shape(q8)
+    cu = check_cu(cu, T)
+    rows, groups = _doc_rows(cu, rows, T)
+    out = {key: np.empty((H, len(rows), D)) for key in ("o", "pbar", "sigma", "acc_bar")}
+    out.update({key: np.empty((H, len(rows))) for key in ("lse", "lse_bar")})
+    for d, (loc, pos) in groups.items():
+        a, b = int(cu[d]), int(cu[d + 1])
+        s0 = first_slot(cu, d, scale_block)
+        sl = slice(s0, s0 + -(-(b - a) // scale_block))
+        res = emulated_fp8_attention_bars(q8[:, a:b], k8[:, a:b], v8[:, a:b], q_descale[:, sl], k_descale[:, sl],
+                                          v_descale[:, sl], scale_block, hadamard, causal, rows=loc, exp2=exp2)
+        for key in out:
+            out[key][:, pos] = res[key]
+    return out
 
 
 def work_items(cu, causal, order="longest_first"):

@@ -4,8 +4,10 @@ oracle (oracle.decode) on the same seeded inputs.
 The cache and the new queries are quantised by quantize_qkv_fp8 on the GPU
 (checked bit-exact against the oracle's quantiser), and the oracle runs its
 own quantiser on the same float inputs.  O and LSE are held to the dense
-path's tolerance (RMSE 2e-3, max-abs 2e-2 + one BF16 ulp + the tie slack of
-P's e4m3 roundings).
+path's contract: E1, the exact attention of the dequantised queries against
+the dequantised cache (no split), within RMSE 2e-3 and max-abs 2e-2 widened
+only by the bars derived from E1 (tests.gpu_common.check_fp8_vs_e1).  The
+kernel-shaped loop with the kernel's split is printed as a diagnostic.
 """
 
 import numpy as np
@@ -16,7 +18,7 @@ import fp8_attention_forward_amd as fa
 import workloads
 from oracle import decode as od
 from oracle import quantize as oq
-from tests.gpu_common import check_fp8_output, dev, host, rms
+from tests.gpu_common import check_fp8_vs_e1, dev, host, rms
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
@@ -54,17 +56,18 @@ def _run(case, seed_off=0):
         assert np.array_equal(host(g), r), f"{nm} codes differ"
     for g, r, nm in ((kd, ref_k[4], "kd"), (vd, ref_k[5], "vd"), (qd, ref_q[3], "qd")):
         assert np.array_equal(host(g).view(np.uint32), r.view(np.uint32)), f"{nm} descales differ"
-    o2, l2, sl = od.emulated_fp8_decode(ref_q[0], ref_q[3], ref_k[1], ref_k[2], ref_k[4], ref_k[5], seqlens, sb, had,
-                                        causal, used, tie_slack=True)
-    return host(o), host(lse), o2, l2, sl, used
+    bars = od.emulated_fp8_decode_bars(ref_q[0], ref_q[3], ref_k[1], ref_k[2], ref_k[4], ref_k[5], seqlens, sb,
+                                       had, causal)
+    o2, _ = od.emulated_fp8_decode(ref_q[0], ref_q[3], ref_k[1], ref_k[2], ref_k[4], ref_k[5], seqlens, sb, had,
+                                   causal, used)
+    return host(o), host(lse), bars, o2, used
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
-def test_decode_matches_emulation(case):
-    o, lse, o2, l2, sl, used = _run(case)
-    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=f"{case[:9]} split {used}", slack=sl)
-    assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5
-    print(f"  split {used}: RMSE vs oracle {r2:.3e} (max {m2:.3e})", flush=True)
+def test_decode_matches_e1(case):
+    o, lse, bars, o2, used = _run(case)
+    check_fp8_vs_e1(o, lse, bars, tag=f"{case[:9]} split {used}")
+    print(f"  split {used}: diagnostic RMSE vs the split loop {rms(o - o2):.3e}", flush=True)
 
 
 def test_decode_run_to_run_bitwise():
@@ -114,10 +117,7 @@ def test_decode_workload_parity(name):
             assert np.array_equal(host(k8[b:b + 1, hk:hk + 1]), ref_k[1])
             assert np.array_equal(host(v8[b:b + 1, hk:hk + 1]), ref_k[2])
             assert np.array_equal(host(q8[b:b + 1, hs]), ref_q[0])
-            o2, l2, sl = od.emulated_fp8_decode(ref_q[0], ref_q[3], ref_k[1], ref_k[2], ref_k[4], ref_k[5],
-                                                seqlens[b:b + 1], w.scale_block, w.hadamard, w.causal, used,
-                                                tie_slack=True)
+            bars = od.emulated_fp8_decode_bars(ref_q[0], ref_q[3], ref_k[1], ref_k[2], ref_k[4], ref_k[5],
+                                               seqlens[b:b + 1], w.scale_block, w.hadamard, w.causal)
             og, lg = host(o[b:b + 1, hs]), host(lse[b:b + 1, hs])
-            r2, m2 = check_fp8_output(og, lg, o2, l2, tag=f"{name} b {b} kv head {hk}", slack=sl)
-            print(f"[{name}] b {b} (L {int(seqlens[b])}) kv head {hk}: RMSE vs oracle {r2:.3e} max {m2:.3e}",
-                  flush=True)
+            check_fp8_vs_e1(og, lg, bars, tag=f"[{name}] b {b} (L {int(seqlens[b])}) kv head {hk}")

@@ -2,9 +2,13 @@
 
 * quantize_qkv_fp8: codes and descales bit-exact against the oracle's float32
   emulation (oracle.quantize).
-* attn_fp8_fwd: O and LSE against exact FP64 attention of the dequantised
-  inputs (oracle.emulated_fp8_attention), within RMSE 2e-3 and max-abs
-  2e-2 + half a BF16 ulp; LSE within 2e-3 * max(1, |LSE|).
+* attn_fp8_fwd (and its options): O and LSE against E1, the exact float64
+  attention of the dequantised inputs (oracle.emulated_fp8_attention): RMSE
+  2e-3, max-abs 2e-2, LSE 2e-3 * max(1, |LSE|), each widened only by the bars
+  that oracle.emulated_fp8_attention_bars derives from E1's own quantities
+  for P's e4m3 rounding, the matrix cores' accumulation and (option)
+  Schraudolph's exponential, plus half a BF16 ulp of the output.  The
+  kernel-shaped loop E2 is printed as a diagnostic.
 * attn_bf16_fwd: against exact FP64 attention of the BF16-rounded inputs.
 
 Small shapes are checked in full; they span several tiles and a ragged tail.
@@ -20,7 +24,7 @@ import fp8_attention_forward_amd as fa
 import workloads
 from oracle import attention as oatt
 from oracle import quantize as oq
-from tests.gpu_common import (bf16_round, check_fp8_output, dev, gpu_quantize, host, rms)
+from tests.gpu_common import bf16_round, check_fp8_vs_e1, dev, gpu_quantize, host, rms
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
@@ -111,35 +115,20 @@ def _fp8_run(q, k, v, sb, had, causal, seed=0x5EED):
 
 
 @pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}".format(*c[:7]))
-def test_attn_fp8_matches_emulated_fp8(case):
+def test_attn_fp8_matches_e1(case):
     B, H, N, D, sb, had, causal, kind = case
     q, k, v = workloads.generate(kind, B, H, N, D, 200 + N)
     o, lse = _fp8_run(q, k, v, sb, had, causal)
     qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED)
-    # the same pipeline emulated (P re-quantised to e4m3 as the kernel does)
-    o2, l2, slk = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, tie_slack=True)
-    if kind == "channel" and not had:
-        # unrotated channel outliers: FP8 MFMA group accumulation error in S
-        # dominates (see LOOSE in test_gpu_workloads)
-        r2, m2 = rms(o - o2), float(np.max(np.abs(o - o2)))
-        assert r2 <= 2e-2 and np.all(np.abs(lse - l2) <= 2e-2 * np.maximum(1.0, np.abs(l2)))
-    else:
-        r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " vs E2", slack=slk)
-        # what is left is the BF16 rounding of O, the FP8 accumulation of the
-        # matrix cores and rare flips of a P rounding
-        assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
-    o1, l1 = oatt.emulated_fp8_attention(*qq, sb, had, causal)
-    r1 = rms(o - o1)
-    print(f"{case}: RMSE vs E2 {r2:.3e} (max {m2:.3e}); vs E1 {r1:.3e}; RMS(O) {rms(o1):.3e}")
+    check_fp8_vs_e1(o, lse, oatt.emulated_fp8_attention_bars(*qq, sb, had, causal), tag=str(case))
+    o2, _ = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal)
+    print(f"{case}: diagnostic RMSE vs E2 {rms(o - o2):.3e}")
 
 
 # Schraudolph's bit-level exponential (attn_fp8_fwd_opts, ATTN_FP8_EXP2_SCHRAUDOLPH)
-# against E2 with the same approximation: the same tolerance again.
-EXP2_CASES = [c for c in ATTN_CASES if not (c[7] == "channel" and not c[5])]
-
-
-@pytest.mark.parametrize("case", EXP2_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}".format(*c[:7]))
-def test_attn_fp8_schraudolph_matches_emulation(case):
+# against E1, with the bars widened by what the approximation can move O and LSE.
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}".format(*c[:7]))
+def test_attn_fp8_schraudolph_matches_e1(case):
     B, H, N, D, sb, had, causal, kind = case
     q, k, v = workloads.generate(kind, B, H, N, D, 200 + N)
     q8, k8, v8, qd, kd, vd = gpu_quantize(q, k, v, sb, had, 0x5EED)
@@ -148,21 +137,19 @@ def test_attn_fp8_schraudolph_matches_emulation(case):
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
     qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED)
-    o2, l2, slk = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2="schraudolph", tie_slack=True)
-    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " schraudolph vs E2", slack=slk)
-    assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
-    oe, _ = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal)
-    print(f"{case}: schraudolph RMSE vs its E2 {r2:.3e} (max {m2:.3e}); vs exact-exp E2 {rms(o - oe):.3e}")
+    check_fp8_vs_e1(o, lse, oatt.emulated_fp8_attention_bars(*qq, sb, had, causal, exp2="schraudolph"),
+                    tag=f"{case} schraudolph")
+    o2, _ = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2="schraudolph")
+    print(f"{case}: diagnostic RMSE vs its E2 {rms(o - o2):.3e}")
 
 
 # Power-of-two block scales applied by the scaled FP8 MFMA (ATTN_FP8_MX), alone
-# and with the Schraudolph exponential, against E2 with the same options.
-MX_CASES = [c + (e,) for c in EXP2_CASES for e in ("exact",)] + \
-    [c + ("schraudolph",) for c in EXP2_CASES[2:5]]
+# and with the Schraudolph exponential, against E1 of the power-of-two codes.
+MX_CASES = [c + ("exact",) for c in ATTN_CASES] + [c + ("schraudolph",) for c in ATTN_CASES[2:5]]
 
 
 @pytest.mark.parametrize("case", MX_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}-{}".format(*c[:7], c[8]))
-def test_attn_fp8_mx_matches_emulation(case):
+def test_attn_fp8_mx_matches_e1(case):
     B, H, N, D, sb, had, causal, kind, exp2 = case
     q, k, v = workloads.generate(kind, B, H, N, D, 300 + N)
     q8, k8, v8, qd, kd, vd = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=sb, hadamard=had,
@@ -172,11 +159,9 @@ def test_attn_fp8_mx_matches_emulation(case):
     torch.cuda.synchronize()
     o, lse = host(o), host(lse)
     qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED, pow2=True)
-    o2, l2, slk = oatt.emulated_fp8_attention_tiled(*qq, sb, had, causal, exp2=exp2, mx=True, tie_slack=True)
-    r2, m2 = check_fp8_output(o, lse, o2, l2, tag=str(case) + " mx vs E2", slack=slk)
-    assert r2 <= 2.0 ** -7 * rms(o2) + 1e-5, f"{case}: RMSE vs E2 {r2:.3e}"
+    check_fp8_vs_e1(o, lse, oatt.emulated_fp8_attention_bars(*qq, sb, had, causal, exp2=exp2), tag=f"{case} mx")
     orf, _ = oatt.reference_attention(q, k, v, causal)
-    print(f"{case}: mx RMSE vs its E2 {r2:.3e} (max {m2:.3e}); vs FP64 {rms(o - orf):.3e}")
+    print(f"{case}: mx RMSE vs FP64 {rms(o - orf):.3e}")
 
 
 BF16_CASES = [

@@ -169,25 +169,32 @@ def test_tiled_fp8_loop_rows_subset():
     assert np.array_equal(o[..., rows, :], o2) and np.array_equal(l[..., rows], l2)
 
 
-def test_tiled_fp8_loop_brute_force_tiny():
+@pytest.mark.parametrize("tau,lift", [(0.0, 0.0), (0.0, 4.0), (8.0, 4.0), (2.0, 1.0)])
+def test_tiled_fp8_loop_brute_force_tiny(tau, lift):
     # two key blocks of 2 keys, d = 4: explicit loops with the stated P rule
+    # (the reference moves to lift below a block's max when that max exceeds
+    # it by more than tau)
     from oracle import e4m3
     rng = np.random.default_rng(34)
     shape = (1, 1, 4, 4)
     q, k, v = (rng.standard_normal(shape).astype(np.float32) for _ in range(3))
+    q[0, 0, 3] *= 8.0                      # a row whose second block moves the reference under every tau
+    k[0, 0, 3] *= 8.0
     qq = quantize.quantize_qkv(q, k, v, 2, False, 0)
     q8, k8, v8, qd, kd, vd = qq
-    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=0.0, bf16_output=False,
+    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=tau, lift=lift, bf16_output=False,
                                                      block_c=2)
     dq = e4m3.decode(q8)[0, 0]
     dk = e4m3.decode(k8)[0, 0]
     dv = e4m3.decode(v8)[0, 0]
     c = math.log2(math.e) / 2.0
     dvref = vd[0, 0].max()
+    moved = 0
     for i in range(4):
         t = [sum(dq[i, x] * dk[j, x] for x in range(4)) * qd[0, 0, i // 2] * kd[0, 0, j // 2] * c for j in range(4)]
-        m0 = max(t[0], t[1])
-        m1 = max(m0, t[2], t[3])
+        m0 = max(t[0], t[1]) - lift
+        m1 = max(t[2], t[3]) - lift if max(t[2], t[3]) > m0 + tau else m0
+        moved += m1 != m0
         num = [0.0] * 4
         for j in range(4):
             mj = m0 if j < 2 else m1
@@ -199,6 +206,7 @@ def test_tiled_fp8_loop_brute_force_tiny():
         for x in range(4):
             assert o[0, 0, i, x] == pytest.approx(num[x] * dvref / l, rel=1e-12, abs=1e-14)
         assert lse[0, 0, i] == pytest.approx(math.log(2) * (m1 + math.log2(l)), rel=1e-12)
+    assert moved >= 1
 
 
 def test_round_to_bf16_matches_torch():
@@ -262,7 +270,7 @@ def test_tiled_mx_loop_brute_force_tiny():
     v[0, 0, 2:] *= 0.1
     qq = quantize.quantize_qkv(q, k, v, 2, False, 0, pow2=True)
     q8, k8, v8, qd, kd, vd = qq
-    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=0.0, bf16_output=False, block_c=2,
+    o, lse = attention.emulated_fp8_attention_tiled(*qq, 2, False, False, tau=0.0, lift=0.0, bf16_output=False, block_c=2,
                                                      mx=True)
     dq, dk, dv = (e4m3.decode(x)[0, 0] for x in (q8, k8, v8))
     c = math.log2(math.e) / 2.0

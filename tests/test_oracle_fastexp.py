@@ -76,16 +76,17 @@ def _codes(shape, seed, scale):
 
 
 def test_e2_schraudolph_single_block_is_brute_force():
-    # one key block and one scale block: m is the row max, r = 1, and the loop
-    # must give O = sum_k S(t_k - m) v_k / sum_k S(t_k - m), LSE = ln 2 (m + log2 sum)
+    # one key block and one scale block: the reference m is the row max less
+    # the lift (4), r = 1, and the loop must give
+    # O = sum_k S(t_k - m) v_k / sum_k S(t_k - m), LSE = ln 2 (m + log2 sum)
     n, d = 64, 64
     q8, k8, v8 = _codes((1, n, d), 1, 40.0), _codes((1, n, d), 2, 40.0), _codes((1, n, d), 3, 40.0)
     qd, kd, vd = np.full((1, 1), 0.02), np.full((1, 1), 0.03), np.full((1, 1), 0.05)
     o, lse = attention.emulated_fp8_attention_tiled(q8, k8, v8, qd, kd, vd, 64, False, False, quantize_p=False,
-                                                    bf16_output=False, block_c=64, exp2="schraudolph")
+                                                    bf16_output=False, block_c=64, exp2="schraudolph", lift=4.0)
     q, k, v = e4m3.decode(q8[0]), e4m3.decode(k8[0]), e4m3.decode(v8[0])
     t = (q @ k.T) * (0.02 * 0.03 * math.log2(math.e) / math.sqrt(d))
-    m = t.max(axis=1)
+    m = t.max(axis=1) - 4.0
     w = schraudolph_exp2(t - m[:, None])
     ob = (w @ (v * 0.05)) / w.sum(axis=1)[:, None]
     lb = math.log(2) * (m + np.log2(w.sum(axis=1)))
@@ -96,8 +97,9 @@ def test_e2_schraudolph_single_block_is_brute_force():
 @pytest.mark.parametrize("causal", [False, True])
 def test_e2_schraudolph_fixed_reference_max(causal):
     # the first key block holds a dominant key for every query, and tau is large,
-    # so the reference max is block 0's max for the whole row; equal V descales
-    # make r = 1.  Then the loop is a plain weighted sum with weights S(t - m0).
+    # so the reference is block 0's max less the lift (4) for the whole row;
+    # equal V descales make r = 1.  Then the loop is a plain weighted sum with
+    # weights S(t - m0).
     n, d, bc = 256, 64, 64
     rng = np.random.default_rng(7)
     q = rng.standard_normal((n, d)) * 20
@@ -109,12 +111,12 @@ def test_e2_schraudolph_fixed_reference_max(causal):
     vd = np.full((1, 4), 0.04)
     o, lse = attention.emulated_fp8_attention_tiled(q8, k8, v8, qd, kd, vd, 64, False, causal, tau=1e4,
                                                     quantize_p=False, bf16_output=False, block_c=bc,
-                                                    exp2="schraudolph")
+                                                    exp2="schraudolph", lift=4.0)
     qq, kk, vv = e4m3.decode(q8[0]), e4m3.decode(k8[0]), e4m3.decode(v8[0]) * 0.04
     t = (qq @ kk.T) * (0.01 * 0.01 * math.log2(math.e) / math.sqrt(d))
     if causal:
         t = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], t, -np.inf)
-    m0 = t[:, :bc].max(axis=1)
+    m0 = t[:, :bc].max(axis=1) - 4.0
     w = schraudolph_exp2(t - m0[:, None])
     ob = (w @ vv) / w.sum(axis=1)[:, None]
     lb = math.log(2) * (m0 + np.log2(w.sum(axis=1)))
