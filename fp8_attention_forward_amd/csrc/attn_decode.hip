@@ -32,8 +32,8 @@
 //     dependent round trips through the splits).
 //
 // Numerics per key range are those of the dense kernel (scale folds, lazy
-// reference max, P = e4m3(2^(t - m) r_j) with r_j relative to the largest V
-// descale of the range, FP32 statistics).
+// reference, P = e4m3(2^(t - m)), V's power-of-two block scale applied inside
+// the matrix core, FP32 statistics).
 #include "common.h"
 #include "attn_internal.h"
 #include "fp8_tiles.h"
@@ -125,18 +125,6 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
     load_v(k0, 0);
   }
 
-  // largest V descale over the blocks of this range (P carries r_j = dv_j /
-  // dvm): one block per lane, then a wave maximum
-  float dvm = 0.0f;
-  if (k0 < k1) {
-    const int b0 = k0 / SB, b1 = (k1 - 1) / SB;
-    for (int blk = b0 + lane; blk <= b1; blk += 64) dvm = fmaxf(dvm, p.vd[(size_t)bk * p.nblk + blk]);
-    dvm = wave_max(dvm);
-  } else {
-    dvm = 1.0f;
-  }
-  const float log2_dvm = __builtin_amdgcn_logf(dvm);
-
   const Fp8LaneOffsets<D> lo(lane);
   v16f o[C::NDT];
 #pragma unroll
@@ -193,10 +181,10 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
     }
-    // P = 2^(t - m + log2 r) in e4m3 (B operand of the P V product), row sum of 2^(t - m)
-    const float dv = vd[blk];
-    const float inv_rv = dvm * __builtin_amdgcn_rcpf(dv);
-    const ExpArgs<kExpExact> ex(c, __builtin_amdgcn_logf(dv) - log2_dvm - m_ref);
+    // P = 2^(t - m) in e4m3 (B operand of the P V product) and its row sum;
+    // V's power-of-two block scale is applied inside the matrix core
+    const int sv = e8m0_of(vd[blk]);
+    const ExpArgs<kExpExact> ex(c, -m_ref);
     float rs = 0.0f;
 #pragma unroll
     for (int sub = 0; sub < C::NSUB; ++sub)
@@ -211,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
         w = cvt_pk_fp8<true>(p2, p3, w);
         pop[4 * sub + a] = w;
       }
-    l_acc = alpha * l_acc + rs * inv_rv;
+    l_acc = alpha * l_acc + rs;
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
@@ -219,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
       const v8i av = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
-      o[dt] = mfma_f8x<false>(av, pop, o[dt], 0, 127);
+      o[dt] = mfma_f8x<true>(av, pop, o[dt], sv, 127);
     }
   }
 
@@ -239,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
   float M = mm[ql];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mm[w * 32 + ql]);
-  const float f = __builtin_amdgcn_exp2f(m_ref - M) * dvm;
+  const float f = __builtin_amdgcn_exp2f(m_ref - M);
   if (wave > 0 && ql < p.MQ) {
     float* mine = slab + ((size_t)(wave - 1) * p.MQ + ql) * D;
 #pragma unroll

@@ -36,9 +36,10 @@
 //     constants), then at most three tail steps for the diagonal and ragged
 //     tiles.
 //   * Scale folding: t = s * (dq * dk_j * score_scale) in log2 units, one FMA
-//     per score with the reference max; V's block scale dv_j enters as the
-//     factor r_j = dv_j / (max dv over the blocks the wave visits) inside the
-//     exponent (so P stays <= 256), and the row sum divides it back out.
+//     per score with the reference max.  V's block scale is a power of two
+//     (the quantiser writes it so) and is applied exactly inside the matrix
+//     core: its E8M0 exponent is the A-operand scale of the P V product, so P
+//     carries no V factor and keeps e4m3's full range.
 //   * Lazy rescale: the reference max only moves when a tile's max exceeds it
 //     by more than kTau (log2 units), so most tiles skip the O rescale; P is
 //     then <= 2^kTau, inside e4m3's range.  With exact exponentials P is
@@ -149,14 +150,17 @@ __device__ __forceinline__ void tile_mask(STile<D>& s, int t, int N, int lane, i
   }
 }
 
-// P of one score tile against the reference max: P = 2^(t - m + log2 r) in
-// e4m3 into pop (the B operand of the P V product); returns this lane's
-// share of the row sum.
+// P of one score tile against the reference: P = 2^(t - m) in e4m3 into pop
+// (the B operand of the P V product).  Returns this lane's share of the row
+// sum; *q4max gets the largest sum of 4 of its P (the exponentials come in
+// fours anyway): when that stays below kMoveBound no single P can exceed
+// 2^kTau, so the reference need not move.
 template <int D, int EXPM>
-__device__ __forceinline__ float p_tile(const STile<D>& s, v8i& pop, float c, float bias) {
+__device__ __forceinline__ float p_tile(const STile<D>& s, v8i& pop, float c, float bias, float* q4max) {
   using C = Fp8Cfg<D>;
   const ExpArgs<EXPM> ex(c, bias);
   float rs = 0.0f;
+  float qm = 0.0f;
 #pragma unroll
   for (int sub = 0; sub < C::NSUB; ++sub)
 #pragma unroll
@@ -165,13 +169,17 @@ __device__ __forceinline__ float p_tile(const STile<D>& s, v8i& pop, float c, fl
       float p1 = ex(s[sub][4 * a + 1]);
       float p2 = ex(s[sub][4 * a + 2]);
       float p3 = ex(s[sub][4 * a + 3]);
-      rs += (p0 + p1) + (p2 + p3);
+      const float q4 = (p0 + p1) + (p2 + p3);
+      rs += q4;
+      // (fmaxf drops a NaN operand: test for it on the sum instead)
+      qm = fmaxf(qm, q4);
       // (the conversion keeps the other half of its destination: start from
       // the previous tile's word, which is dead by now)
       int w = cvt_pk_fp8<false>(p0, p1, pop[4 * sub + a]);
       w = cvt_pk_fp8<true>(p2, p3, w);
       pop[4 * sub + a] = w;
     }
+  *q4max = rs == rs ? qm : rs;
   return rs;
 }
 
@@ -202,9 +210,9 @@ __device__ __forceinline__ bool move_reference(const STile<D>& s, Fp8State<D>& s
   return true;
 }
 
-// Largest normalised P (P / r <= 2^tau) the reference allows without moving,
-// less a margin for the rounding of the exponent argument (|m| < 2^14).
-constexpr float kMoveBound = 256.0f * (1.0f - 1.0f / 64.0f);
+// Largest P (<= 2^kTau) the reference allows without moving, less a margin
+// for the rounding of the exponent argument (|m| < 2^14).
+constexpr float kMoveBound = 445.7218f * (1.0f - 1.0f / 64.0f);
 
 // One pipelined step in two phases with the workgroup barrier between them.
 // On entry S_t (masked) is ready.  Phase A turns S_t into P_t (exponentials,
@@ -215,32 +223,31 @@ constexpr float kMoveBound = 256.0f * (1.0f - 1.0f / 64.0f);
 // which keeps the registers low enough for three waves per SIMD: the latency
 // one wave waits on, the others fill.
 //
-// Exact exponentials: the reference moves only when some P_t / r_t would
-// exceed 2^tau against it, and the row sum bounds every P.  So P_t is formed
-// against the current reference first, and the tile maximum is taken only
-// when some lane's normalised row sum reaches kMoveBound (rarely once the
-// reference has settled; always on the first tile, whose reference is -1e30
-// and whose P overflow to +inf).  When the reference does move, P_t is formed
-// again, and each P is then at most r_t.  The decisions are those of taking
+// Exact exponentials: the reference moves only when some P_t would exceed
+// 2^tau against it, and a sum of four P bounds each of them.  So P_t is
+// formed against the current reference first, and the tile maximum is taken
+// only when one of some lane's sums of four reaches kMoveBound (rarely once
+// the reference has settled; always on the first tile, whose reference is
+// -1e30 and whose P overflow to +inf).  When the reference does move, P_t is
+// formed again, and each P is then at most 2^kLift.  The decisions are those of taking
 // the maximum of every tile.  Schraudolph's exponential cannot be formed
 // first: past 2^128 its bits run into the sign field instead of saturating,
 // so there the maximum is taken before the exponentials, on every tile.
-template <int D, int EXPM, bool MX>
-__device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, float c, float inv_rv,
-                                           float log2_rv) {
+template <int D, int EXPM>
+__device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, float c) {
   float alpha = 1.0f;
-  float rs;
+  float rs, q4;
   if constexpr (EXPM == kExpExact) {
-    rs = p_tile<D, EXPM>(s, st.pop, c, log2_rv - st.m_ref);
-    // (written so that a NaN sum also counts)
-    if (__builtin_amdgcn_ballot_w64(!(rs * inv_rv <= kMoveBound))) {
-      if (move_reference<D>(s, st, c, alpha)) rs = p_tile<D, EXPM>(s, st.pop, c, log2_rv - st.m_ref);
+    rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
+    // (written so that a NaN also counts)
+    if (__builtin_amdgcn_ballot_w64(!(q4 <= kMoveBound))) {
+      if (move_reference<D>(s, st, c, alpha)) rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
     }
   } else {
     move_reference<D>(s, st, c, alpha);
-    rs = p_tile<D, EXPM>(s, st.pop, c, log2_rv - st.m_ref);
+    rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
   }
-  st.l_acc = alpha * st.l_acc + rs * inv_rv;
+  st.l_acc = alpha * st.l_acc + rs;
 }
 
 template <int D, bool CAUSAL, bool MASK_NEXT, bool MX>
@@ -256,7 +263,7 @@ __device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, con
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
       const v8i a = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
-      st.o[dt] = mfma_f8x<MX>(a, st.pop, st.o[dt], sv, 127);
+      st.o[dt] = mfma_f8x<true>(a, st.pop, st.o[dt], sv, 127);
     }
   }
   // (a tile this wave will not visit must not move the reference max)
@@ -344,16 +351,6 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   const int rows_wg = N < n_kt_wg * kBC ? N : n_kt_wg * kBC;
   const uint32_t lim = (uint32_t)rows_wg * D;
 
-  // largest V block scale over the key blocks this wave visits (for causal calls
-  // only blocks up to the wave's own, so no output depends on a later block)
-  float dvm = 1.0f;
-  if constexpr (!MX) {
-    dvm = 0.0f;
-    for (int b = lane; b <= kt_w / TPB; b += 64) dvm = fmaxf(dvm, seq.vd[b]);
-    dvm = wave_max(dvm);
-  }
-  const float log2_dvm = __builtin_amdgcn_logf(dvm);
-
   const Fp8LaneOffsets<D> lo(lane);
   const Fp8Dma<D> dma(wave, lane, lds_addr_of(smem));
   Fp8State<D> st;
@@ -365,12 +362,10 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
 
   // per-tile score scale
   auto c_of = [&](int t) { return MX ? c_q : c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
-  // E8M0 exponents of a tile's K and V block scales (MX only)
+  // E8M0 exponents of a tile's K block scale (MX only) and V block scale (a
+  // power of two in every mode)
   auto sk_of = [&](int t) { return MX ? e8m0_of(kd[(t < n_kt ? t : n_kt - 1) / TPB]) : 0; };
-  auto sv_of = [&](int t) { return MX ? e8m0_of(vd[(t < n_kt ? t : n_kt - 1) / TPB]) : 0; };
-  // factor 1/r and log2 r of a tile's V block (r = dv / dvm; 1 and 0 with MX)
-  auto ir_of = [&](float dv) { return MX ? 1.0f : dvm * __builtin_amdgcn_rcpf(dv); };
-  auto lr_of = [&](float dv) { return MX ? 0.0f : __builtin_amdgcn_logf(dv) - log2_dvm; };
+  auto sv_of = [&](int t) { return e8m0_of(vd[(t < n_kt ? t : n_kt - 1) / TPB]); };
   constexpr uint32_t KS = 0, VS = kRing * C::TILE;   // ring bases (byte offsets in smem)
 
   // prologue: K0, K1, K2, V0, V1 resident; S_0 (masked)
@@ -402,8 +397,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
       t = tt;                                                                                        \
       break;                                                                                         \
     }                                                                                                \
-    const float dv = vd[tt / TPB];                                                                   \
-    fp8_phaseA<D, EXPM, MX>(s, st, c_of(tt), ir_of(dv), lr_of(dv));                                  \
+    fp8_phaseA<D, EXPM>(s, st, c_of(tt));                                                            \
     wait_vmem_prev_step<2 * C::CHUNKS_PER_WAVE>();                                                   \
     workgroup_barrier();                                                                             \
     issue_tile<D, false>(kh8, lim, tt + 3, KS + (KF) * C::TILE, dma);                                \
@@ -424,8 +418,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   // compiler schedules in this part.
   for (; t < n_kt_wg; ++t) {
     const bool active = t <= kt_w;
-    const float dv = vd[t / TPB];
-    if (active) fp8_phaseA<D, EXPM, MX>(s, st, c_of(t), ir_of(dv), lr_of(dv));
+    if (active) fp8_phaseA<D, EXPM>(s, st, c_of(t));
     wait_vmem_all();
     workgroup_barrier();
     issue_tile<D, false>(kh8, lim, t + 3, KS + (t % kRing) * C::TILE, dma);
@@ -436,9 +429,9 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   }
   wait_vmem_all();   // no tile load may still be writing LDS when the workgroup ends
 
-  // ---- epilogue: O = dvm * O_acc / l ; LSE = ln 2 * (m + log2 l)
+  // ---- epilogue: O = O_acc / l ; LSE = ln 2 * (m + log2 l)
   const float l_tot = st.l_acc + swap_halves(st.l_acc);
-  const float inv_l = dvm / l_tot;
+  const float inv_l = 1.0f / l_tot;
   if (my_q < N) {
     uint16_t* orow = seq.o + (size_t)my_q * D;
 #pragma unroll

@@ -8,12 +8,15 @@
 
 namespace attnfp8 {
 
-constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units): P <= 2^8
+// Lazy-rescale threshold (log2 units): P <= 2^kTau ~ 445.7, just inside
+// e4m3's largest value 448 (and below 464, from where the convert would
+// overflow, even with Schraudolph's +2% error).
+constexpr float kTau = 8.8f;
 // When the reference moves it is set kLift below the tile maximum (log2
 // units, a whole number): the key that moved it gets P = 2^kLift, which e4m3
-// holds exactly, while the small probabilities sit 2^kLift higher, away from
-// e4m3's subnormal range.  Moves still happen only when some P would exceed
-// 2^kTau, so P <= 256 as before.
+// holds exactly, and the small probabilities sit 2^kLift higher, away from
+// e4m3's subnormal range.  The headroom kTau - kLift decides how closely the
+// reference follows the running maximum.
 constexpr float kLift = 4.0f;
 
 // Exponentials of the probabilities P.

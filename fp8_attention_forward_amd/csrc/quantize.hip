@@ -1,9 +1,9 @@
 // Fused rotate + per-block scale + e4m3 encode of Q, K and V (gfx950).
 //
 // Method ("Fused attention kernel", Variants / 8-bit forward pass (FP8)):
-// every block of Q, K and V gets its own scale, and Q and K are first
-// multiplied by a random sign diagonal times a Hadamard matrix (incoherent
-// processing), which cancels in Q K^T.  FLAMIA (4.3 Ablation Study) fuses the
+// scales are per block, separately for Q, K and V, and Q and K are first
+// rotated by a random +-1 diagonal times a Hadamard matrix (incoherent
+// processing); the rotation is orthogonal, so Q K^T is unchanged.  FLAMIA (4.3 Ablation Study) fuses the
 // quantisation pre-processing into a single launch; here one launch covers
 // all three tensors.
 //
@@ -16,8 +16,10 @@
 // amax over the block (wave + LDS reduction), inv = 448/a and descale = a/448
 // (correctly rounded), and code = e4m3(clamp(y * inv, +-448)) with the
 // hardware round-to-nearest-even convert; one 4-byte store per lane per row.
-// With power-of-two scales (the microscaling form, FLAMIA 2 Background) the
-// descale is the smallest 2^e that keeps the block's amax inside +-448.
+// V's blocks, and with the power-of-two option (the microscaling form, FLAMIA
+// 2 Background) every block, take the smallest 2^e that keeps the block's
+// amax inside +-448: the attention applies such a scale exactly inside the
+// matrix core.
 //
 // Memory: reads 4 B and writes 1 B per element (HBM bound), both with
 // non-temporal accesses (each byte is touched once).
@@ -75,9 +77,9 @@ __device__ __forceinline__ float exp2i(int e) {
 // One scale block: rows [0, nrows) (nrows <= SB) of src, D floats each ->
 // e4m3 codes at dst (same row layout) and the block's descale at *dsc.
 // Called by every thread of the workgroup (it holds a workgroup barrier).
-template <int D, int SB, bool POW2>
+template <int D, int SB>
 __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, int nrows, float* dsc, bool rotate,
-                                               uint32_t key0, uint32_t key1) {
+                                               bool pow2, uint32_t key0, uint32_t key1) {
 #pragma clang fp contract(off)
   constexpr int LPR = D / 4;              // lanes per row
   constexpr int RPI = 256 / LPR;          // rows per iteration (whole workgroup)
@@ -143,7 +145,7 @@ __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, i
   __syncthreads();
   const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float inv, descale;
-  if constexpr (POW2) {
+  if (pow2) {
     const int e = pow2_scale_exponent(a);
     inv = exp2i(-e);
     descale = exp2i(e);
@@ -177,8 +179,8 @@ __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
   const int row0 = blk * SB;
   const size_t off = ((size_t)bh * p.N + row0) * D;
   const int nrows = p.N - row0 < SB ? p.N - row0 : SB;
-  quantize_block<D, SB, POW2>(src + off, dst + off, nrows, dsc + (size_t)bh * p.nblk + blk,
-                              p.hadamard && tensor < 2, p.key0, p.key1);
+  quantize_block<D, SB>(src + off, dst + off, nrows, dsc + (size_t)bh * p.nblk + blk, p.hadamard && tensor < 2,
+                        POW2 || tensor == 2, p.key0, p.key1);
 }
 
 // Packed documents ("FLAMIA", Abstract and 4.1 Performance on Packed
@@ -228,8 +230,8 @@ __global__ __launch_bounds__(256) void quantize_qkv_varlen_kernel(QuantVarlenPar
   float* dsc = tensor == 0 ? p.qd : (tensor == 1 ? p.kd : p.vd);
   const size_t off = ((size_t)h * p.T + r0) * D;
   const int nrows = b - r0 < SB ? b - r0 : SB;
-  quantize_block<D, SB, POW2>(src + off, dst + off, nrows, dsc + (size_t)h * p.nslot + g,
-                              p.hadamard && tensor < 2, p.key0, p.key1);
+  quantize_block<D, SB>(src + off, dst + off, nrows, dsc + (size_t)h * p.nslot + g, p.hadamard && tensor < 2,
+                        POW2 || tensor == 2, p.key0, p.key1);
 }
 
 #define QUANT_INST(D, SB) \

@@ -4,9 +4,9 @@
  * "Fused attention kernel" (wikillm.com), sections "Overview" and
  * "Implementation sketch", fed by the 8-bit pre-processing of its section
  * "Variants / 8-bit forward pass (FP8, Hopper)": incoherent processing (Q and
- * K multiplied by a random sign diagonal times a Hadamard matrix, which cancels
- * in Q K^T) and block quantisation to e4m3 with one scale per block of Q, K and
- * V.  The problem page "FP8 attention that keeps FlashAttention-3 throughput at
+ * K rotated by a random +-1 diagonal times a Hadamard matrix, an orthogonal
+ * transform that leaves Q K^T unchanged) and e4m3 quantisation with a scale
+ * chosen per block, separately for Q, K and V.  The problem page "FP8 attention that keeps FlashAttention-3 throughput at
  * BF16-level accuracy", section "How it gets verified", fixes the types: Q, K, V
  * in E4M3, FP32 softmax statistics, BF16 output; and measures the FP8 error
  * against the BF16 forward pass, exported here as attn_bf16_fwd.
@@ -50,7 +50,8 @@ typedef enum {
 /* quantize_qkv_fp8 -- rotate + per-block scale + e4m3 encode of Q, K and V in
  * one launch ("Fused attention kernel", 8-bit forward pass: block quantisation
  * and incoherent processing; fused into one launch as in FLAMIA, 4.3 Ablation
- * Study).
+ * Study).  V's block scales are powers of two (the attention applies them
+ * exactly inside the matrix core); Q's and K's map the block maximum to 448.
  *   q, k, v        in : float32 [B][H][N][D].
  *   scale_block       : tokens per scale block (64 or 128); a block is
  *                       scale_block consecutive tokens of one (batch, head)
@@ -62,11 +63,15 @@ typedef enum {
  *                       counter 0 and key (seed low word, seed high word);
  *                       sigma_c = -1 when bit c of the 128-bit output is set.
  *   q8, k8, v8    out : e4m3 codes [B][H][N][D], code = e4m3_rne(clamp(y * inv, +-448))
- *   q/k/v_descale out : float32 [B][H][ceil(N/scale_block)], descale = amax/448
+ *   q/k_descale   out : float32 [B][H][ceil(N/scale_block)], descale = amax/448
  *                       (inv = 448/amax; 1 for an all-zero block).  A nonzero
  *                       block amax below 448 / FLT_MAX (about 1.3e-36) makes
  *                       inv overflow and is outside the contract of this rule
  *                       (the power-of-two rule of ATTN_FP8_MX covers it).
+ *   v_descale     out : float32 [B][H][ceil(N/scale_block)], the smallest power
+ *                       of two 2^e with amax <= 448 * 2^e (e clamped to
+ *                       [-127, 127]; 2^0 for an all-zero block): an E8M0
+ *                       scale, inv = 2^-e exactly, no code saturates.
  */
 int quantize_qkv_fp8(const float* q, const float* k, const float* v,
                      int B, int H, int N, int D, int scale_block, int hadamard, uint64_t seed,
@@ -104,13 +109,17 @@ int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v,
  *   q8, k8, v8, *_descale in : output of quantize_qkv_fp8 with the same
  *                       scale_block and hadamard flag (hadamard nonzero folds
  *                       the 1/D of the unnormalised rotation into the score
- *                       scale).
+ *                       scale).  v_descale must hold powers of two: only
+ *                       their exponent fields are read, as the E8M0 scale of
+ *                       the P V product (v_mfma_scale_f32_32x32x64_f8f6f4).
  *   causal            : nonzero -> query i sees keys j <= i.
  *   o_bf16        out : bf16 bit patterns [B][H][N][D],
  *                       O = softmax(Q K^T / sqrt(D)) V of the dequantised inputs.
  *   lse           out : float32 [B][H][N], natural log of sum_j exp(q_i.k_j / sqrt(D)).
  * Arithmetic: e4m3 x e4m3 products with FP32 accumulation, FP32 statistics,
- * P re-quantised to e4m3 on chip.
+ * P re-quantised to e4m3 on chip (P = 2^(t - m) <= 256 against a per-row
+ * reference m, which moves only when a key block would exceed 256, and then
+ * to 2^4 below that block's maximum).
  */
 int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  const float* q_descale, const float* k_descale, const float* v_descale,
@@ -287,7 +296,7 @@ const char* attn_fp8_last_error(void);
 /* ABI version of this header (incremented on incompatible changes). */
 int attn_fp8_abi_version(void);
 
-#define ATTN_FP8_ABI_VERSION 3
+#define ATTN_FP8_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

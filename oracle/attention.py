@@ -99,14 +99,13 @@ def emulated_fp8_attention(q8, k8, v8, q_descale, k_descale, v_descale,
 # quantised inputs) with three departures that the pages fix or leave open,
 # each bounded here from E1's own quantities (scores, weights, codes,
 # descales), never from a kernel's blocking:
-#   * P is rounded to e4m3 before its product with V ([P1] / north-star
-#     reading C12; the pages do not model it).  A probability P in e4m3 moves
-#     by at most 2^-4 P (normal range) or min(P, 2^-10) (subnormal range, in
-#     units where the row's largest P is at least 1).  The V block scale,
-#     when it is folded into P, is at most the largest V descale of the
-#     sequence.  So |dO_id| <= sum_j [2^-4 w_ij |v_jd|
-#     + min(w_ij |v_jd|, 2^-10 dv_max |V8_jd| / l_i)], l_i the row sum against
-#     the row maximum (l_i >= 1).
+#   * P is rounded to e4m3 before its product with V (reading C12; the pages
+#     do not model it).  A probability P in e4m3 moves by at most 2^-4 P
+#     (normal range) or min(P, 2^-10) (subnormal range), in units where the
+#     row's largest P is at least 1 (P carries no V factor: V's power-of-two
+#     scale is applied to V).  So |dO_id| <= sum_j [2^-4 w_ij
+#     + min(w_ij, 2^-10 / l_i)] |v_jd|, l_i the row sum against the row
+#     maximum (l_i >= 1).
 #   * The matrix cores sum the e4m3 products with the truncation of
 #     ``mfma_fp8``: each score moves by at most delta_ij (natural units);
 #     a row whose scores all move by at most D_i has its log-sum-exp moved by
@@ -164,7 +163,6 @@ def e1_rows_with_bars(q8r, dq, k8, dk, v8, dv, q_pos, causal, scale, exp2, accum
     w = p / l[:, None]
     o = w @ vv
     lse = m + np.log(l)
-    dvmax = float(np.max(dv))
     wabs = w @ np.abs(vv)
     # sum_j w_ij |v_jd - O_id|, row by row
     wdev = np.empty_like(o)
@@ -195,14 +193,13 @@ def e1_rows_with_bars(q8r, dq, k8, dk, v8, dv, q_pos, causal, scale, exp2, accum
         grow = np.ones(len(m))
         lse_acc = np.zeros(len(m))
     # P below e4m3's normal range: its rounding error is at most the smaller
-    # of P itself and half the smallest subnormal
-    cap = 2.0 ** -10 * dvmax / l
+    # of P itself and half the smallest subnormal (P = w l, l >= 1)
+    cap = 2.0 ** -10 / l
     absvv = np.abs(vv)
-    absv8m = np.abs(v8v)
     sub = np.empty_like(o)
     sub2 = np.empty_like(o)
     for i in range(o.shape[0]):
-        t = np.minimum(w[i][:, None] * absvv, cap[i] * absv8m)
+        t = np.minimum(w[i], cap[i])[:, None] * absvv
         sub[i] = t.sum(axis=0)
         sub2[i] = (t * t).sum(axis=0)
     var = (2.0 ** -8 / 3.0) * ((w * w) @ (vv * vv)) + sub2 / 3.0
@@ -210,7 +207,7 @@ def e1_rows_with_bars(q8r, dq, k8, dk, v8, dv, q_pos, causal, scale, exp2, accum
     if exp2 == "exact":
         pbar = 2.0 ** -4 * wabs + sub
     elif exp2 == "schraudolph":
-        pbar = ETA * wdev + 2.0 ** -4 * (1.0 + ETA) * wabs + sub / (1.0 + EPS_LO)
+        pbar = ETA * wdev + (2.0 ** -4 * wabs + sub) * (1.0 + ETA)
         dev2 = np.empty_like(o)
         for i in range(o.shape[0]):
             dev2[i] = (w[i] * w[i]) @ (vv - o[i]) ** 2
@@ -318,48 +315,28 @@ def brute_force_attention(q, k, v, causal, scale):
     return np.array(o), np.array(lse)
 
 
-# Relative half-width of the window around an e4m3 rounding midpoint inside
-# which a probability evaluated in float32 (its exponent argument carries a
-# few float32 roundings of scores up to a few hundred in log2 units, and the
-# hardware exponential is within one ulp) can round to either neighbour.
-P_TIE_WINDOW = 2.0 ** -14
-
-
-def e4m3_tie_step(x, window=P_TIE_WINDOW):
-    """For x >= 0: the e4m3 spacing at x where x lies within ``window * x`` of
-    a rounding midpoint (so either neighbour is a valid rounding at a lower
-    precision), else 0."""
-    x = np.asarray(x, dtype=np.float64)
-    _, fexp = np.frexp(np.where(x > 0, x, 1.0))
-    quantum = np.ldexp(1.0, np.maximum(fexp - 1, -6) - 3)
-    frac = x / quantum - np.floor(x / quantum)
-    near = (x > 0) & (np.abs(frac - 0.5) * quantum <= window * x)
-    return np.where(near, quantum, 0.0)
-
-
 def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
-                                 causal, rows=None, tau=8.0, quantize_p=True, bf16_output=True, block_c=64,
-                                 exp2="exact", mx=False, tie_slack=False, lift=4.0):
-    """E2: the running-softmax loop over key blocks with P re-quantised to e4m3.
+                                 causal, rows=None, tau=8.8, quantize_p=True, bf16_output=True, block_c=64,
+                                 exp2="exact", lift=4.0):
+    """E2 (a diagnostic, not the contract): the running-softmax loop over key
+    blocks with P re-quantised to e4m3, in the FP8 kernel's blocking.
 
     The pages fix the loop (Implementation sketch) and that the matrix products
     run on 8-bit inputs; they are silent on the precision and scale of P.
-    Reading taken here (the FP8 kernel follows it):
-      * the loop visits key blocks of ``block_c`` keys (the sketch's block_c;
-        64 in the kernel), which must divide ``scale_block``; scores in log2
-        units: t = s * dq_i * dk_j * log2(e) / sqrt(d) (/ d if rotated), where s
-        is the exact dot product of the decoded codes and dk_j the descale of
-        the scale block holding key block j;
+    Readings taken here (the FP8 kernel follows them):
+      * the loop visits key blocks of ``block_c`` keys (64 in the kernel),
+        which must divide ``scale_block``; scores in log2 units:
+        t = s * dq_i * dk_j * log2(e) / sqrt(d) (/ d if rotated), s the exact
+        dot product of the decoded codes, dk_j the descale of key block j;
       * a reference m is kept per query; it moves only when a block's max
         exceeds m by more than ``tau``, and then to ``lift`` (a whole number)
         below that max, so the key that moved it has P = 2^lift exactly; with
         tau = lift = 0 this is the sketch's running max;
-      * P entering the product with V is e4m3(2^(t - m) * r_j) with
-        r_j = dv_j / dv_ref, dv_ref the largest V descale among the key blocks
-        that the query's block can see (all blocks when not causal); so P <= 2^tau;
-      * the old partial output is multiplied by 2^(m_old - m_new) when m moves
-        (the sketch's exp(old max - new max));
-      * l sums the unquantised 2^(t - m); O = dv_ref * O_acc / l;
+      * P = e4m3(2^(t - m)) <= 2^tau enters the product with V, whose
+        (power-of-two) block scale multiplies V itself (the matrix core
+        applies it); the old partial output is multiplied by 2^(m_old - m_new)
+        when m moves (the sketch's exp(old max - new max));
+      * l sums the unquantised 2^(t - m); O = O_acc / l;
         LSE = ln 2 * (m + log2 l), the natural log-sum-exp of the scaled scores;
       * O is delivered in BF16 ([P1] "How it gets verified": BF16 output),
         rounded to nearest even (``bf16_output``); LSE stays float64.
@@ -368,24 +345,9 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     equals E1 up to float64 rounding.
 
     ``exp2="schraudolph"`` replaces the probabilities' exponential by
-    Schraudolph's bit-level approximation (``fastexp.schraudolph_exp2``), taken
-    of the whole exponent t - m + log2 r_j, as the kernel's option does:
-    P = e4m3(S(t - m + log2 r_j)) and l sums S(t - m + log2 r_j) / r_j.  The
-    rescale 2^(m_old - m_new) stays exact.
-
-    ``mx=True`` (power-of-two descales applied to the operands by the matrix
-    units): V's block scale multiplies V itself, so P = e4m3(2^(t - m)) carries
-    no r_j (dv_ref = 1), and O = O_acc / l with O_acc = sum P (v * dv_j).  With
-    power-of-two scales this differs from the default only where e4m3 rounding
-    of 2^(t-m) r_j and of 2^(t-m) differ (subnormal P).
-
-    ``tie_slack=True`` also returns, per output element, how far O can move
-    when every P whose unrounded value lies within ``P_TIE_WINDOW`` of an
-    e4m3 rounding midpoint (``e4m3_tie_step``) rounds to its other neighbour:
-    the sum of those rounding steps times |v| (dequantised), carried through
-    the rescales and the final normalisation like O itself.  It is the part of
-    a lower-precision evaluation's difference that is a valid rounding, not an
-    error.  Returns (O, LSE, slack) then.
+    Schraudolph's bit-level approximation (``fastexp.schraudolph_exp2``) of
+    t - m, as the kernel's option does: P = e4m3(S(t - m)) and l sums
+    S(t - m).  The rescale 2^(m_old - m_new) stays exact.
     """
     if exp2 not in ("exact", "schraudolph"):
         raise ValueError("exp2 must be 'exact' or 'schraudolph'")
@@ -404,21 +366,12 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     nkb = -(-n // block_c)
     o_all = np.empty(lead + (len(row_idx), d))
     lse_all = np.empty(lead + (len(row_idx),))
-    slack_all = np.zeros(lead + (len(row_idx), d))
     for idx in np.ndindex(*lead):
         qh, kh, vh = q[idx][row_idx], k[idx], v[idx]
         qdr = qd[idx][row_idx // scale_block]
-        own_blk = row_idx // scale_block
-        if mx:
-            dv_ref = np.ones(len(row_idx))
-        elif causal:
-            dv_ref = np.array([vd[idx][:b + 1].max() for b in own_blk])
-        else:
-            dv_ref = np.full(len(row_idx), vd[idx].max())
         m = np.full(len(row_idx), -np.inf)
         l = np.zeros(len(row_idx))
         acc = np.zeros((len(row_idx), d))
-        slk = np.zeros((len(row_idx), d))
         for j in range(nkb):
             k0, k1 = j * block_c, min(n, (j + 1) * block_c)
             sb = k0 // scale_block
@@ -432,30 +385,16 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
             alpha = np.where(upd, np.exp2(np.where(np.isfinite(m), m - m_new, -np.inf)), 1.0)
             m = m_new
             ok = np.isfinite(m)
-            r = np.ones(len(row_idx)) if mx else vd[idx][sb] / dv_ref
-            if exp2 == "exact":
-                pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
-                pu[~ok] = 0.0
-                pq = pu * r[:, None]
-            else:
-                pq = fastexp.schraudolph_exp2(t - np.where(ok, m, 0.0)[:, None] + np.log2(r)[:, None])
-                pq[~ok] = 0.0
-                pu = pq / r[:, None]
-            vblk = vh[k0:k1] * (vd[idx][sb] if mx else 1.0)
-            if tie_slack:
-                slk = alpha[:, None] * slk + (e4m3_tie_step(pq) if quantize_p else 0.0 * pq) @ np.abs(vblk)
-            if quantize_p:
-                pq = e4m3.decode(e4m3.encode(pq))
+            arg = t - np.where(ok, m, 0.0)[:, None]
+            pu = np.exp2(arg) if exp2 == "exact" else fastexp.schraudolph_exp2(arg)
+            pu[~ok] = 0.0
+            pq = e4m3.decode(e4m3.encode(pu)) if quantize_p else pu
             l = alpha * l + pu.sum(axis=1)
-            acc = alpha[:, None] * acc + pq @ vblk
-        o_all[idx] = acc * dv_ref[:, None] / l[:, None]
+            acc = alpha[:, None] * acc + pq @ (vh[k0:k1] * vd[idx][sb])
+        o_all[idx] = acc / l[:, None]
         lse_all[idx] = math.log(2.0) * (m + np.log2(l))
-        if tie_slack:
-            slack_all[idx] = slk * dv_ref[:, None] / l[:, None]
     if bf16_output:
         o_all = round_to_bf16(o_all)
-    if tie_slack:
-        return o_all, lse_all, slack_all
     return o_all, lse_all
 
 

@@ -19,10 +19,9 @@ The pages give no decode algorithm.  Readings taken here:
   * the keys are split into ranges of ``split`` consecutive keys (a multiple
     of the 64-key tile).  Each range runs the E2 loop of ``attention`` on its
     own: tiles of 64 keys, the lazy reference (threshold tau, moved to
-    ``lift`` below the block maximum),
-    P = e4m3(2^(t - m) r_j) with r_j = dv_j / dv_ref and dv_ref the largest V
-    descale of the scale blocks the range touches, l summing the unrounded
-    2^(t - m); it yields (m, l, O^ = dv_ref * sum P v).  The ranges merge
+    ``lift`` below the block maximum), P = e4m3(2^(t - m)) against V scaled
+    by its power-of-two block descale, l summing the unrounded 2^(t - m); it
+    yields (m, l, O^ = sum P v).  The ranges merge
     exactly: M = max m, w = 2^(m - M), O = sum w O^ / sum w l,
     LSE = ln 2 (M + log2 sum w l).  Without the rounding of P, the split
     changes nothing but rounding order;
@@ -34,18 +33,17 @@ import math
 import numpy as np
 
 from . import e4m3
-from .attention import e1_rows_with_bars, e4m3_tie_step, round_to_bf16
+from .attention import e1_rows_with_bars, round_to_bf16
 
 TILE = 64
 
 
 def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_block, hadamard, causal,
-                        split, tau=8.0, quantize_p=True, bf16_output=True, tie_slack=False, lift=4.0):
-    """Decode of [B][Hq][Sq][D] query codes against the FP8 cache.  Returns
-    (O [B][Hq][Sq][D], LSE [B][Hq][Sq]) in float64 (O rounded to BF16 values
-    unless ``bf16_output`` is False) and, with ``tie_slack``, the movement of
-    O that valid lower-precision roundings of P allow (``attention.e4m3_tie_step``,
-    carried like O)."""
+                        split, tau=8.8, quantize_p=True, bf16_output=True, lift=4.0):
+    """Decode of [B][Hq][Sq][D] query codes against the FP8 cache, in the
+    kernel's key ranges (a diagnostic; the contract is E1,
+    ``emulated_fp8_decode_bars``).  Returns (O [B][Hq][Sq][D], LSE [B][Hq][Sq])
+    in float64 (O rounded to BF16 values unless ``bf16_output`` is False)."""
     if split % TILE or scale_block % TILE:
         raise ValueError("split and scale_block must be multiples of 64")
     B, Hq, Sq, D = np.shape(q8)
@@ -62,7 +60,6 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
     score_scale = math.log2(math.e) / math.sqrt(D) / (D if hadamard else 1)
     o = np.zeros((B, Hq, Sq, D))
     lse = np.zeros((B, Hq, Sq))
-    slack = np.zeros((B, Hq, Sq, D))
     for b in range(B):
         L = int(seqlens[b])
         if not Sq <= L <= np.shape(k8)[2]:
@@ -75,11 +72,9 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
             parts = []
             for r0 in range(0, L, split):
                 r1 = min(L, r0 + split)
-                dv_ref = vd[b, g, r0 // scale_block:(r1 - 1) // scale_block + 1].max()
                 m = np.full(Sq, -np.inf)
                 l = np.zeros(Sq)
                 acc = np.zeros((Sq, D))
-                slk = np.zeros((Sq, D))
                 for k0 in range(r0, r1, TILE):
                     k1 = min(r1, k0 + TILE)
                     blk = k0 // scale_block
@@ -95,25 +90,18 @@ def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, sc
                     ok = np.isfinite(m)
                     pu = np.exp2(t - np.where(ok, m, 0.0)[:, None])
                     pu[~ok] = 0.0
-                    pq = pu * (vd[b, g, blk] / dv_ref)
-                    if tie_slack and quantize_p:
-                        slk = alpha[:, None] * slk + e4m3_tie_step(pq) @ np.abs(vv[b, g, k0:k1])
-                    if quantize_p:
-                        pq = e4m3.decode(e4m3.encode(pq))
+                    pq = e4m3.decode(e4m3.encode(pu)) if quantize_p else pu
                     l = alpha * l + pu.sum(axis=1)
-                    acc = alpha[:, None] * acc + pq @ vv[b, g, k0:k1]
-                parts.append((m, l, acc * dv_ref, slk * dv_ref))
+                    acc = alpha[:, None] * acc + pq @ (vv[b, g, k0:k1] * vd[b, g, blk])
+                parts.append((m, l, acc))
             M = np.max([p[0] for p in parts], axis=0)
             w = [np.where(np.isfinite(p[0]), np.exp2(p[0] - M), 0.0) for p in parts]
             lt = sum(wi * p[1] for wi, p in zip(w, parts))
             ot = sum(wi[:, None] * p[2] for wi, p in zip(w, parts))
             o[b, h] = ot / lt[:, None]
             lse[b, h] = math.log(2.0) * (M + np.log2(lt))
-            slack[b, h] = sum(wi[:, None] * p[3] for wi, p in zip(w, parts)) / lt[:, None]
     if bf16_output:
         o = round_to_bf16(o)
-    if tie_slack:
-        return o, lse, slack
     return o, lse
 
 

@@ -1,8 +1,10 @@
 """Sylvester Hadamard matrix and its fast transform (oracle; test infrastructure only).
 
 [P2] "Fused attention kernel", Variants / 8-bit forward pass: Q and K are
-multiplied by an orthogonal matrix made of a random sign diagonal and a
-Hadamard matrix; because it cancels in Q K^T the output is unchanged.
+rotated by the same orthogonal transform, a random +-1 diagonal followed by a
+Hadamard matrix; an orthogonal transform applied to both leaves every dot
+product q . k, and so the attention output, unchanged in exact arithmetic,
+while it spreads a large channel over all channels.
 
 Readings taken here (the pages do not fix them):
   * The Hadamard matrix is Sylvester's, in natural order:

@@ -1,11 +1,10 @@
 """Rotate + per-block scale + e4m3 encode of Q, K, V (oracle; test infrastructure only).
 
 [P2] "Fused attention kernel", Variants / 8-bit forward pass (FP8, Hopper):
-  * block quantisation: every block of Q, K and V gets its own scale instead of
-    one scale per tensor;
-  * incoherent processing: Q and K (not V) are multiplied by an orthogonal
-    matrix, a random sign diagonal times a Hadamard matrix, before they are
-    quantised.
+  * scales are chosen per block, separately for Q, K and V, rather than once
+    for a whole tensor;
+  * before Q and K (never V) are quantised they are rotated by one orthogonal
+    transform: a random +-1 diagonal followed by a Hadamard matrix.
 [P3] FLAMIA, 4.3 Ablation Study: quantisation fused into one launch, and score
 scales folded together (the 1/d of the unnormalised Hadamard and the block
 descales fold into the score scale on the attention side).
@@ -21,6 +20,11 @@ Readings taken here:
   * code = e4m3(fl32(y * inv)) with the encoder of ``oracle.e4m3``;
   * rotation: y = x * sigma (exact), then the float32 fast Walsh-Hadamard
     transform of ``oracle.hadamard`` (unnormalised, stage order fixed).
+  * V's blocks take the power-of-two form below in every mode: an e4m3 code
+    has the same relative precision at any power-of-two scale, and such a
+    scale is applied exactly inside the matrix core that forms P V, so P
+    need not carry V's scale (the kernel then keeps P away from e4m3's
+    subnormal range).
 Dequantised value: e4m3_value(code) * descale.
 
 Power-of-two (microscaling, E8M0) scales, the option ``pow2=True`` ([P3]
@@ -102,13 +106,15 @@ def quantize_qkv(q, k, v, scale_block, hadamard, seed, pow2=False):
     """The full pre-processing of one attention call.
 
     Returns (q8, k8, v8, q_descale, k_descale, v_descale).  Q and K share one
-    sign vector drawn from ``seed``; V is never rotated.
+    sign vector drawn from ``seed``; V is never rotated.  V's blocks always
+    take power-of-two scales (the product with P applies them exactly);
+    ``pow2`` gives Q and K power-of-two scales too.
     """
     d = np.shape(q)[-1]
     signs = sign_vector(seed, d) if hadamard else None
     q8, qd = quantize_tensor(q, scale_block, signs, pow2)
     k8, kd = quantize_tensor(k, scale_block, signs, pow2)
-    v8, vd = quantize_tensor(v, scale_block, None, pow2)
+    v8, vd = quantize_tensor(v, scale_block, None, True)
     return q8, k8, v8, qd, kd, vd
 
 

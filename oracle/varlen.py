@@ -117,15 +117,13 @@ def emulated_fp8_attention_varlen(q8, k8, v8, q_descale, k_descale, v_descale, c
 
     Each document is a sequence of its own: its codes, and the descales of its
     blocks read from its slots.  Keyword options (tau, quantize_p, bf16_output,
-    block_c, exp2, mx, tie_slack) pass through.  Returns (O [H, R, D], LSE
-    [H, R]) and, with tie_slack, the slack [H, R, D].
+    block_c, exp2, lift) pass through.  Returns (O [H, R, D], LSE [H, R]).
     """
     H, T, D = np.shape(q8)
     cu = check_cu(cu, T)
     rows, groups = _doc_rows(cu, rows, T)
     o = np.empty((H, len(rows), D))
     lse = np.empty((H, len(rows)))
-    slack = np.zeros((H, len(rows), D))
     for d, (loc, pos) in groups.items():
         a, b = int(cu[d]), int(cu[d + 1])
         s0 = first_slot(cu, d, scale_block)
@@ -136,10 +134,6 @@ def emulated_fp8_attention_varlen(q8, k8, v8, q_descale, k_descale, v_descale, c
                                            rows=loc, **kw)
         o[:, pos] = res[0]
         lse[:, pos] = res[1]
-        if kw.get("tie_slack"):
-            slack[:, pos] = res[2]
-    if kw.get("tie_slack"):
-        return o, lse, slack
     return o, lse
 
 

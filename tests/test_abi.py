@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert fa.abi_version() == 3
+    assert fa.abi_version() == 4
     m = re.search(r"#define ATTN_FP8_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == fa.abi_version()
 

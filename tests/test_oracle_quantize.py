@@ -108,7 +108,8 @@ def test_quantize_qkv_rotates_q_and_k_only():
     signs = sign_vector(0x5EED, 64)
     assert np.array_equal(out[0], quantize.quantize_tensor(q, 64, signs)[0])
     assert np.array_equal(out[1], quantize.quantize_tensor(k, 64, signs)[0])
-    assert np.array_equal(out[2], quantize.quantize_tensor(v, 64, None)[0])
+    assert np.array_equal(out[2], quantize.quantize_tensor(v, 64, None, pow2=True)[0])   # V: power-of-two scales
+    assert np.array_equal(out[5], quantize.quantize_tensor(v, 64, None, pow2=True)[1])
     assert out[3].shape == (1, 2, 3) and out[5].dtype == np.float32
     off = quantize.quantize_qkv(q, k, v, 64, False, 0x5EED)
     assert np.array_equal(off[0], quantize.quantize_tensor(q, 64, None)[0])
