@@ -32,7 +32,8 @@ __all__ = [
     "last_error", "abi_version", "EXPORTED_SYMBOLS", "ATTN_OK", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EHIP",
     "ATTN_FP8_EXP2_SCHRAUDOLPH", "ATTN_FP8_MX", "ATTN_FP8_NATURAL_ORDER", "EXP2_MODES", "ORDERS",
     "quantize_qkv_fp8_varlen", "attn_fp8_fwd_varlen", "attn_fp8_varlen_workspace_bytes", "varlen_num_slots",
-    "attn_fp8_decode", "attn_fp8_decode_workspace_bytes", "attn_fp8_decode_split",
+    "attn_fp8_decode", "attn_fp8_decode_workspace_bytes", "attn_fp8_decode_split", "attn_fp8_decode_noalloc",
+    "DECODE_NOALLOC_MAX_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_fp8.so")
@@ -45,6 +46,7 @@ EXP2_MODES = {"exact": 0, "schraudolph": ATTN_FP8_EXP2_SCHRAUDOLPH}
 EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "quantize_qkv_fp8_opts", "attn_fp8_fwd", "attn_fp8_fwd_opts", "attn_bf16_fwd",
                     "quantize_qkv_fp8_varlen", "attn_fp8_varlen_workspace_bytes", "attn_fp8_fwd_varlen",
                     "attn_fp8_decode_split", "attn_fp8_decode_workspace_bytes", "attn_fp8_decode",
+                    "attn_fp8_decode_noalloc",
                     "attn_fp8_last_error", "attn_fp8_abi_version")
 
 _lib = None
@@ -93,6 +95,8 @@ def load_library(path=None):
     lib.attn_fp8_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                     vp, ctypes.c_size_t, vp, vp, vp]
     lib.attn_fp8_decode.restype = i32
+    lib.attn_fp8_decode_noalloc.argtypes = [vp] * 7 + [i32] * 10 + [vp] * 3
+    lib.attn_fp8_decode_noalloc.restype = i32
     lib.attn_fp8_last_error.argtypes = []
     lib.attn_fp8_last_error.restype = ctypes.c_char_p
     lib.attn_fp8_abi_version.argtypes = []
@@ -327,6 +331,9 @@ def attn_fp8_decode_workspace_bytes(B, Hq, Hkv, Sq, Ncap, D, split=0):
                                                               int(split)))
 
 
+DECODE_NOALLOC_MAX_BYTES = 16 << 20       # ATTN_FP8_DECODE_NOALLOC_MAX_BYTES
+
+
 def attn_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_block=128, hadamard=True,
                     causal=True, split=0, out=None, workspace=None):
     """Decode: q8 [B, Hq, Sq, D] uint8 with q_descale [B, Hq] or [B, Hq, 1]; cache k8, v8 [B, Hkv, Ncap, D]
@@ -364,4 +371,34 @@ def attn_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_
         int(scale_block), int(bool(hadamard)), int(bool(causal)), int(split), _ptr(workspace, torch.uint8, "workspace"),
         ctypes.c_size_t(workspace.numel()), _ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"),
         _stream(q8)))
+    return out
+
+
+def attn_fp8_decode_noalloc(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, out, scale_block=128,
+                            hadamard=True, causal=True, split=0):
+    """attn_fp8_decode with no workspace and no allocation: the partials live in the
+    library's per-GPU scratch array (see include/attn_fp8.h).  ``out`` = (o, lse) must be
+    given (o [B, Hq, Sq, D] bfloat16, lse [B, Hq, Sq] float32); returns it."""
+    lib = load_library()
+    B, Hq, Sq, D = _shape4(q8, "q8")
+    Bk, Hkv, Ncap, Dk = _shape4(k8, "k8")
+    if (Bk, Dk) != (B, D) or _shape4(v8, "v8") != (B, Hkv, Ncap, D):
+        raise ValueError("k8 / v8 must be [B, Hkv, Ncap, D] with the queries' B and D")
+    if tuple(q_descale.shape) not in ((B, Hq), (B, Hq, 1)):
+        raise ValueError("q_descale must be [B, Hq] (or [B, Hq, 1])")
+    nb = -(-Ncap // scale_block)
+    for t, nm in ((k_descale, "k_descale"), (v_descale, "v_descale")):
+        if tuple(t.shape) != (B, Hkv, nb):
+            raise ValueError(f"{nm} must be [B, Hkv, ceil(Ncap / scale_block)]")
+    if seqlens.dim() != 1 or seqlens.numel() != B:
+        raise ValueError("seqlens must be [B]")
+    o, lse = out
+    if _shape4(o, "o") != (B, Hq, Sq, D) or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("o / lse have the wrong shape")
+    _check(lib.attn_fp8_decode_noalloc(
+        _ptr(q8, torch.uint8, "q8"), _ptr(q_descale, torch.float32, "q_descale"), _ptr(k8, torch.uint8, "k8"),
+        _ptr(v8, torch.uint8, "v8"), _ptr(k_descale, torch.float32, "k_descale"),
+        _ptr(v_descale, torch.float32, "v_descale"), _ptr(seqlens, torch.int32, "seqlens"), B, Hq, Hkv, Sq, Ncap, D,
+        int(scale_block), int(bool(hadamard)), int(bool(causal)), int(split), _ptr(o, torch.bfloat16, "o"),
+        _ptr(lse, torch.float32, "lse"), _stream(q8)))
     return out

@@ -46,6 +46,36 @@ int check_device() {
   return ATTN_OK;
 }
 
+// Scratch memory of attn_fp8_decode_noalloc: the per-range partials that
+// attn_fp8_decode keeps in the caller's workspace.  One copy per GPU the
+// library runs on, held until the process ends; every call on a GPU shares
+// it (calls that overlap on one GPU race).  The host-side name `scratch` is
+// only a stand-in: kernels get the device address that hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kDecodeScratchBytes = ATTN_FP8_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];   // device address of `scratch` per device, looked up once
+
+// Device address of this device's `scratch` (the current device must be a
+// checked gfx950).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(ATTN_EHIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(ATTN_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return ATTN_OK;
+}
+
 int check_sizes(int B, int H, int N, int D) {
   if (B < 1 || H < 1 || N < 1) return fail(ATTN_EINVAL, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
   if (D != 64 && D != 128) return fail(ATTN_EINVAL, "D must be 64 or 128 (got %d)", D);
@@ -305,10 +335,14 @@ size_t attn_fp8_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Ncap,
   return (size_t)((long long)B * Hkv * nsplit * mq * (D + 2) * 4);
 }
 
-int attn_fp8_decode(const uint8_t* q8, const float* q_descale, const uint8_t* k8, const uint8_t* v8,
-                    const float* k_descale, const float* v_descale, const int32_t* seqlens, int B, int Hq, int Hkv,
-                    int Sq, int Ncap, int D, int scale_block, int hadamard, int causal, int split, void* workspace,
-                    size_t workspace_bytes, uint16_t* o_bf16, float* lse, void* stream) {
+}  // extern "C"
+
+// The decode with its partials in `workspace`, or (use_scratch) in the
+// library's own scratch array.
+static int decode_impl(const uint8_t* q8, const float* q_descale, const uint8_t* k8, const uint8_t* v8,
+                       const float* k_descale, const float* v_descale, const int32_t* seqlens, int B, int Hq, int Hkv,
+                       int Sq, int Ncap, int D, int scale_block, int hadamard, int causal, int split, void* workspace,
+                       size_t workspace_bytes, bool use_scratch, uint16_t* o_bf16, float* lse, void* stream) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Ncap < 1)
     return fail(ATTN_EINVAL, "B, Hq, Hkv, Sq, Ncap must be >= 1 (got %d, %d, %d, %d, %d)", B, Hq, Hkv, Sq, Ncap);
   if (D != 64 && D != 128) return fail(ATTN_EINVAL, "D must be 64 or 128 (got %d)", D);
@@ -328,13 +362,19 @@ int attn_fp8_decode(const uint8_t* q8, const float* q_descale, const uint8_t* k8
   CHECK(check_ptr(k_descale, 4, "k_descale"));
   CHECK(check_ptr(v_descale, 4, "v_descale"));
   CHECK(check_ptr(seqlens, 4, "seqlens"));
-  CHECK(check_ptr(workspace, 16, "workspace"));
+  if (!use_scratch) CHECK(check_ptr(workspace, 16, "workspace"));
   CHECK(check_ptr(o_bf16, 16, "o_bf16"));
   CHECK(check_ptr(lse, 4, "lse"));
   const size_t need = attn_fp8_decode_workspace_bytes(B, Hq, Hkv, Sq, Ncap, D, split);
-  if (workspace_bytes < need)
+  if (use_scratch) {
+    if (need > kDecodeScratchBytes)
+      return fail(ATTN_EINVAL, "these sizes need %zu bytes of partials, more than the %zu bytes of scratch the "
+                  "library holds per GPU (attn_fp8_decode takes a workspace of any size)", need, kDecodeScratchBytes);
+  } else if (workspace_bytes < need) {
     return fail(ATTN_EINVAL, "workspace_bytes %zu < %zu (attn_fp8_decode_workspace_bytes)", workspace_bytes, need);
+  }
   CHECK(check_device());
+  if (use_scratch) CHECK(scratch_address(&workspace));
   attnfp8::DecodeParams p;
   p.q8 = q8; p.qd = q_descale;
   p.k8 = k8; p.v8 = v8; p.kd = k_descale; p.vd = v_descale;
@@ -354,6 +394,24 @@ int attn_fp8_decode(const uint8_t* q8, const float* q_descale, const uint8_t* k8
   p.score_scale = (float)sc;
   return launched(attnfp8::launch_attn_fp8_decode(p, D, scale_block, causal ? 1 : 0, (hipStream_t)stream),
                   "attn_fp8_decode");
+}
+
+extern "C" {
+
+int attn_fp8_decode(const uint8_t* q8, const float* q_descale, const uint8_t* k8, const uint8_t* v8,
+                    const float* k_descale, const float* v_descale, const int32_t* seqlens, int B, int Hq, int Hkv,
+                    int Sq, int Ncap, int D, int scale_block, int hadamard, int causal, int split, void* workspace,
+                    size_t workspace_bytes, uint16_t* o_bf16, float* lse, void* stream) {
+  return decode_impl(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, B, Hq, Hkv, Sq, Ncap, D, scale_block,
+                     hadamard, causal, split, workspace, workspace_bytes, false, o_bf16, lse, stream);
+}
+
+int attn_fp8_decode_noalloc(const uint8_t* q8, const float* q_descale, const uint8_t* k8, const uint8_t* v8,
+                            const float* k_descale, const float* v_descale, const int32_t* seqlens, int B, int Hq,
+                            int Hkv, int Sq, int Ncap, int D, int scale_block, int hadamard, int causal, int split,
+                            uint16_t* o_bf16, float* lse, void* stream) {
+  return decode_impl(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, B, Hq, Hkv, Sq, Ncap, D, scale_block,
+                     hadamard, causal, split, nullptr, 0, true, o_bf16, lse, stream);
 }
 
 int attn_fp8_decode_split(int B, int Hkv, int Ncap, int split) {

@@ -289,6 +289,27 @@ int attn_fp8_decode(const uint8_t* q8, const float* q_descale,
                     void* workspace, size_t workspace_bytes,
                     uint16_t* o_bf16, float* lse, void* stream);
 
+/* attn_fp8_decode_noalloc -- attn_fp8_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace: the per-range
+ * partials live in a scratch array of ATTN_FP8_DECODE_NOALLOC_MAX_BYTES that
+ * the library holds on every GPU it runs on until the process ends (a
+ * file-scope __device__ array; no hipMalloc, hipFree or other allocation
+ * happens in the call).  Sizes whose partials
+ * (attn_fp8_decode_workspace_bytes(...)) exceed that limit -> ATTN_EINVAL,
+ * nothing launched.  Every call on one GPU shares its array and leaves its
+ * partials there (nothing in it needs clearing: each call writes every
+ * partial it reads): calls that overlap on one GPU, on different streams or
+ * threads, race and must not be made.  Other arguments, outputs and errors
+ * as for attn_fp8_decode; the result is bitwise the same. */
+#define ATTN_FP8_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+int attn_fp8_decode_noalloc(const uint8_t* q8, const float* q_descale,
+                            const uint8_t* k8, const uint8_t* v8,
+                            const float* k_descale, const float* v_descale,
+                            const int32_t* seqlens, int B, int Hq, int Hkv, int Sq, int Ncap, int D,
+                            int scale_block, int hadamard, int causal, int split,
+                            uint16_t* o_bf16, float* lse, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none).
  * The string is owned by the library and valid until the next call on that thread. */
 const char* attn_fp8_last_error(void);
