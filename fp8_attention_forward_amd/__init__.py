@@ -30,7 +30,7 @@ import torch
 __all__ = [
     "LIB_PATH", "AttnError", "load_library", "quantize_qkv_fp8", "attn_fp8_fwd", "attn_bf16_fwd",
     "last_error", "abi_version", "EXPORTED_SYMBOLS", "ATTN_OK", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EHIP",
-    "ATTN_FP8_EXP2_SCHRAUDOLPH", "ATTN_FP8_MX", "ATTN_FP8_NATURAL_ORDER", "EXP2_MODES", "ORDERS",
+    "ATTN_FP8_EXP2_SCHRAUDOLPH", "ATTN_FP8_MX", "ATTN_FP8_MX32", "ATTN_FP8_NATURAL_ORDER", "EXP2_MODES", "ORDERS",
     "quantize_qkv_fp8_varlen", "attn_fp8_fwd_varlen", "attn_fp8_varlen_workspace_bytes", "varlen_num_slots",
     "attn_fp8_decode", "attn_fp8_decode_workspace_bytes", "attn_fp8_decode_split", "attn_fp8_decode_noalloc",
     "DECODE_NOALLOC_MAX_BYTES",
@@ -41,6 +41,7 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_FP8_EXP2_SCHRAUDOLPH = 1
 ATTN_FP8_MX = 2
 ATTN_FP8_NATURAL_ORDER = 4
+ATTN_FP8_MX32 = 8
 ORDERS = {"longest_first": 0, "natural": ATTN_FP8_NATURAL_ORDER}
 EXP2_MODES = {"exact": 0, "schraudolph": ATTN_FP8_EXP2_SCHRAUDOLPH}
 EXPORTED_SYMBOLS = ("quantize_qkv_fp8", "quantize_qkv_fp8_opts", "attn_fp8_fwd", "attn_fp8_fwd_opts", "attn_bf16_fwd",
@@ -141,47 +142,50 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED, out=None, mx=False):
+def quantize_qkv_fp8(q, k, v, scale_block=128, hadamard=True, seed=0x5EED, out=None, mx=False, mx32=False):
     """Rotate (Q, K) + per-block scale + e4m3 encode; returns (q8, k8, v8, q_descale, k_descale, v_descale).
 
     mx=True: power-of-two (E8M0) block scales (quantize_qkv_fp8_opts with ATTN_FP8_MX).
+    mx32=True: one power-of-two scale per block x 32 channels (ATTN_FP8_MX32); descales [B, H, nblk, D / 32].
     """
     lib = load_library()
     B, H, N, D = _shape4(q, "q")
     if _shape4(k, "k") != (B, H, N, D) or _shape4(v, "v") != (B, H, N, D):
         raise ValueError("q, k, v must have the same shape")
     nb = -(-N // scale_block)
+    dshape = (B, H, nb, D // 32) if mx32 else (B, H, nb)
     if out is None:
         dev = q.device
         out = tuple(torch.empty((B, H, N, D), dtype=torch.uint8, device=dev) for _ in range(3)) + \
-            tuple(torch.empty((B, H, nb), dtype=torch.float32, device=dev) for _ in range(3))
+            tuple(torch.empty(dshape, dtype=torch.float32, device=dev) for _ in range(3))
     q8, k8, v8, qd, kd, vd = out
     for t, nm in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
         if _shape4(t, nm) != (B, H, N, D):
             raise ValueError(f"{nm} has the wrong shape")
     for t, nm in ((qd, "q_descale"), (kd, "k_descale"), (vd, "v_descale")):
-        if tuple(t.shape) != (B, H, nb):
-            raise ValueError(f"{nm} must be [B, H, ceil(N/scale_block)]")
+        if tuple(t.shape) != dshape:
+            raise ValueError(f"{nm} must be {list(dshape)}")
     head = (_ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
             B, H, N, D, int(scale_block), int(bool(hadamard)), int(seed) & 0xFFFFFFFFFFFFFFFF)
     tail = (_ptr(q8, torch.uint8, "q8"), _ptr(k8, torch.uint8, "k8"), _ptr(v8, torch.uint8, "v8"),
             _ptr(qd, torch.float32, "q_descale"), _ptr(kd, torch.float32, "k_descale"),
             _ptr(vd, torch.float32, "v_descale"), _stream(q))
-    if mx:
-        _check(lib.quantize_qkv_fp8_opts(*head, ATTN_FP8_MX, *tail))
+    if mx or mx32:
+        _check(lib.quantize_qkv_fp8_opts(*head, ATTN_FP8_MX32 if mx32 else ATTN_FP8_MX, *tail))
     else:
         _check(lib.quantize_qkv_fp8(*head, *tail))
     return out
 
 
 def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, hadamard=True,
-                 causal=False, out=None, exp2="exact", mx=False):
+                 causal=False, out=None, exp2="exact", mx=False, mx32=False):
     """FP8 attention forward; returns (o [B,H,N,D] bfloat16, lse [B,H,N] float32).
 
     exp2: "exact" or "schraudolph" (ATTN_FP8_EXP2_SCHRAUDOLPH: bit-level
     exponentials for the probabilities).  mx=True: power-of-two descales
-    applied by the matrix cores (ATTN_FP8_MX).  Any option goes through
-    attn_fp8_fwd_opts, none through attn_fp8_fwd.
+    applied by the matrix cores (ATTN_FP8_MX); mx32=True: the same per 32
+    channels (ATTN_FP8_MX32, descales [B, H, nblk, D / 32]).  Any option goes
+    through attn_fp8_fwd_opts, none through attn_fp8_fwd.
     """
     lib = load_library()
     if exp2 not in EXP2_MODES:
@@ -190,9 +194,10 @@ def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, h
     if _shape4(k8, "k8") != (B, H, N, D) or _shape4(v8, "v8") != (B, H, N, D):
         raise ValueError("q8, k8, v8 must have the same shape")
     nb = -(-N // scale_block)
+    dshape = (B, H, nb, D // 32) if mx32 else (B, H, nb)
     for t, nm in ((q_descale, "q_descale"), (k_descale, "k_descale"), (v_descale, "v_descale")):
-        if tuple(t.shape) != (B, H, nb):
-            raise ValueError(f"{nm} must be [B, H, ceil(N/scale_block)]")
+        if tuple(t.shape) != dshape:
+            raise ValueError(f"{nm} must be {list(dshape)}")
     if out is None:
         out = (torch.empty((B, H, N, D), dtype=torch.bfloat16, device=q8.device),
                torch.empty((B, H, N), dtype=torch.float32, device=q8.device))
@@ -204,7 +209,7 @@ def attn_fp8_fwd(q8, k8, v8, q_descale, k_descale, v_descale, scale_block=128, h
             _ptr(v_descale, torch.float32, "v_descale"), B, H, N, D, int(scale_block), int(bool(hadamard)),
             int(bool(causal)))
     tail = (_ptr(o, torch.bfloat16, "o"), _ptr(lse, torch.float32, "lse"), _stream(q8))
-    flags = EXP2_MODES[exp2] | (ATTN_FP8_MX if mx else 0)
+    flags = EXP2_MODES[exp2] | (ATTN_FP8_MX32 if mx32 else (ATTN_FP8_MX if mx else 0))
     if flags == 0:
         _check(lib.attn_fp8_fwd(*args, *tail))
     else:

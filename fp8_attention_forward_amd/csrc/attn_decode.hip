@@ -77,8 +77,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
   v8i qop[C::KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < C::KSTEPS; ++ks) {
-    const v4i lo4 = *(const v4i*)(p.q8 + qrow * D + 64 * ks + 32 * h);
-    const v4i hi4 = *(const v4i*)(p.q8 + qrow * D + 64 * ks + 32 * h + 16);
+    const v4i lo4 = *(const v4i*)(p.q8 + qrow * D + op_channel(ks, h, 0));
+    const v4i hi4 = *(const v4i*)(p.q8 + qrow * D + op_channel(ks, h, 1));
     qop[ks] = (v8i){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
   }
   const float c_q = p.qd[(size_t)b * p.Hq + hq] * p.score_scale;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
           kc.r[sub][ks][half] = __builtin_bit_cast(
-              v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, (t + sub * 32 + ql) * D + 64 * ks + 32 * h + 16 * half,
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, (t + sub * 32 + ql) * D + op_channel(ks, h, half),
                                                          0, 0));
   };
   auto load_v = [&](int t, int buf) {
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
     // S^T = K Q^T
     STile<D> s;
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) s[sub] = qk_mfma<D, false>(kc, qop, sub, 0, 0);
+    for (int sub = 0; sub < C::NSUB; ++sub) s[sub] = qk_mfma<D, false>(kc, qop, sub, KsScales<D>{}, KsScales<D>{});
     if (t + kBC < k1) load_k(t + kBC);
     const int blk = t / SB;
     const float c = c_q * kd[blk];

@@ -100,7 +100,8 @@ __device__ __forceinline__ void issue_tile(const uint8_t* head, uint32_t lim_byt
 // S^T of one tile: 32 keys x 32 queries per subtile
 template <int D, bool MX>
 __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const Fp8LaneOffsets<D>& lo,
-                                        const v8i (&qop)[Fp8Cfg<D>::KSTEPS], STile<D>& s, int sk, int sq) {
+                                        const v8i (&qop)[Fp8Cfg<D>::KSTEPS], STile<D>& s, const KsScales<D>& sk,
+                                        const KsScales<D>& sq) {
   KOps<D> k;
   read_k<D>(kbuf, lo, k);
 #pragma unroll
@@ -250,11 +251,18 @@ __device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, f
   st.l_acc = alpha * st.l_acc + rs;
 }
 
+// V's scale operands of the P V product, one per 32-row d-tile (E8M0)
+template <int D>
+struct DtScales {
+  int v[Fp8Cfg<D>::NDT];
+};
+
 template <int D, bool CAUSAL, bool MASK_NEXT, bool MX>
 __device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, const uint8_t* knext,
                                            const Fp8LaneOffsets<D>& lo, const v8i (&qop)[Fp8Cfg<D>::KSTEPS],
                                            Fp8State<D>& st, int t, int N, int lane, int iw, int my_q,
-                                           bool pv_active, bool next_valid, int sv, int sk_next, int sq) {
+                                           bool pv_active, bool next_valid, const DtScales<D>& sv,
+                                           const KsScales<D>& sk_next, const KsScales<D>& sq) {
   using C = Fp8Cfg<D>;
   if (!MASK_NEXT || pv_active) {
 #pragma unroll
@@ -263,7 +271,7 @@ __device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, con
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
       const v8i a = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
-      st.o[dt] = mfma_f8x<true>(a, st.pop, st.o[dt], sv, 127);
+      st.o[dt] = mfma_f8x<true>(a, st.pop, st.o[dt], sv.v[dt], 127);
     }
   }
   // (a tile this wave will not visit must not move the reference max)
@@ -277,7 +285,7 @@ __device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, con
         const v4i a0 = lds_read_b128(knext + sub * 32 * D + lo.k[ks][0]);
         const v4i a1 = lds_read_b128(knext + sub * 32 * D + lo.k[ks][1]);
         const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        acc = mfma_f8x<MX>(a, qop[ks], acc, sk_next, sq);
+        acc = mfma_f8x<MX>(a, qop[ks], acc, sk_next.v[ks], sq.v[ks]);
       }
       s[sub] = acc;
     }
@@ -288,8 +296,12 @@ __device__ __forceinline__ void fp8_phaseB(STile<D>& s, const uint8_t* vcur, con
 // One query tile (128 queries) of one sequence: the whole loop.  The view
 // holds the sequence's rows (a head of the dense layout, or one document of a
 // packed head), its block descales and its output rows.
-template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
+// GRP = 32 (with MX): one power-of-two scale per 32 channels of a block, the
+// descales of block b at [b * D / 32, (b + 1) * D / 32).
+template <int D, int SB, bool CAUSAL, int EXPM, bool MX, int GRP = 0>
 __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
+  static_assert(GRP == 0 || (GRP == 32 && MX), "32-channel scales are power-of-two scales");
+  constexpr int NG = GRP == 0 ? 1 : D / GRP;   // descales per block
   using C = Fp8Cfg<D>;
   constexpr int TPB = SB / kBC;   // key tiles per scale block
   // three-slot rings for K (slots 0..2) and V (slots 3..5): a tile arrives two
@@ -311,15 +323,15 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   const cfloat* kd = (const cfloat*)seq.kd;
   const cfloat* vd = (const cfloat*)seq.vd;
 
-  // queries of this lane as the B operand: Q[q][64ks + 32h .. +31]
+  // queries of this lane as the B operand: Q[q][op_channel(ks, h, 0..1) .. +15]
   v8i qop[C::KSTEPS];
   {
     const int qrow = my_q < N ? my_q : N - 1;
     const uint8_t* qp = seq.q8 + (size_t)qrow * D;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
-      v4i lo = *(const v4i*)(qp + 64 * ks + 32 * h);
-      v4i hi = *(const v4i*)(qp + 64 * ks + 32 * h + 16);
+      v4i lo = *(const v4i*)(qp + op_channel(ks, h, 0));
+      v4i hi = *(const v4i*)(qp + op_channel(ks, h, 1));
       qop[ks] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
@@ -330,7 +342,19 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   // sq, sk, sv), so the score scale is the constant score_scale and V needs no
   // fold into P
   const float c_q = MX ? seq.score_scale : seq.qd[qblk] * seq.score_scale;
-  const int sq = MX ? e8m0_of(seq.qd[qblk]) : 0;
+  KsScales<D> sq;
+#pragma unroll
+  for (int ks = 0; ks < C::KSTEPS; ++ks) {
+    if constexpr (GRP == 0) {
+      sq.v[ks] = MX ? e8m0_of(seq.qd[qblk]) : 0;
+    } else {
+      // the scale of lane half h covers k-block h of K-step ks: channels
+      // 64 ks + 32 h .. + 31, group 2 ks + h (op_channel puts them there)
+      const int lo_e = e8m0_of(seq.qd[qblk * NG + 2 * ks]);
+      const int hi_e = e8m0_of(seq.qd[qblk * NG + 2 * ks + 1]);
+      sq.v[ks] = h ? hi_e : lo_e;
+    }
+  }
 
   const int n_kt = (N + kBC - 1) / kBC;
   int n_kt_wg = n_kt;              // key tiles the workgroup steps through
@@ -364,8 +388,28 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   auto c_of = [&](int t) { return MX ? c_q : c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
   // E8M0 exponents of a tile's K block scale (MX only) and V block scale (a
   // power of two in every mode)
-  auto sk_of = [&](int t) { return MX ? e8m0_of(kd[(t < n_kt ? t : n_kt - 1) / TPB]) : 0; };
-  auto sv_of = [&](int t) { return e8m0_of(vd[(t < n_kt ? t : n_kt - 1) / TPB]); };
+  auto sk_of = [&](int t) {
+    KsScales<D> r;
+    const int b = (t < n_kt ? t : n_kt - 1) / TPB;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      if constexpr (GRP == 0) {
+        r.v[ks] = MX ? e8m0_of(kd[b]) : 0;
+      } else {
+        const int lo_e = e8m0_of(kd[b * NG + 2 * ks]);
+        const int hi_e = e8m0_of(kd[b * NG + 2 * ks + 1]);
+        r.v[ks] = h ? hi_e : lo_e;
+      }
+    }
+    return r;
+  };
+  auto sv_of = [&](int t) {
+    DtScales<D> r;
+    const int b = (t < n_kt ? t : n_kt - 1) / TPB;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) r.v[dt] = e8m0_of(vd[b * NG + (GRP == 0 ? 0 : dt)]);
+    return r;
+  };
   constexpr uint32_t KS = 0, VS = kRing * C::TILE;   // ring bases (byte offsets in smem)
 
   // prologue: K0, K1, K2, V0, V1 resident; S_0 (masked)
@@ -448,7 +492,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
 }
 
 // Dense layout: one workgroup per (batch x head, query tile).
-template <int D, int SB, bool CAUSAL, int EXPM, bool MX>
+template <int D, int SB, bool CAUSAL, int EXPM, bool MX, int GRP = 0>
 __global__ __launch_bounds__(256, 3) void attn_fp8_kernel(AttnFp8Params p) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   // (the division runs on the vector ALU: bring the uniform results back to
@@ -461,14 +505,15 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_kernel(AttnFp8Params p) {
   seq.q8 = p.q8 + head;
   seq.k8 = p.k8 + head;
   seq.v8 = p.v8 + head;
-  seq.qd = p.qd + (size_t)bh * p.nblk;
-  seq.kd = p.kd + (size_t)bh * p.nblk;
-  seq.vd = p.vd + (size_t)bh * p.nblk;
+  constexpr int NG = GRP == 0 ? 1 : D / GRP;
+  seq.qd = p.qd + (size_t)bh * p.nblk * NG;
+  seq.kd = p.kd + (size_t)bh * p.nblk * NG;
+  seq.vd = p.vd + (size_t)bh * p.nblk * NG;
   seq.o = p.o + head;
   seq.lse = p.lse + (size_t)bh * p.N;
   seq.N = p.N;
   seq.score_scale = p.score_scale;
-  attn_fp8_seq<D, SB, CAUSAL, EXPM, MX>(seq, qt);
+  attn_fp8_seq<D, SB, CAUSAL, EXPM, MX, GRP>(seq, qt);
 }
 
 // Packed documents ("FLAMIA", Abstract and 4.1 Performance on Packed
@@ -506,7 +551,9 @@ __global__ __launch_bounds__(256, 3) void attn_fp8_varlen_kernel(AttnFp8VarlenPa
   template __global__ void attn_fp8_varlen_kernel<D, SB, CA, E, MX>(AttnFp8VarlenParams);
 #define FP8_INST_E(D, SB, CA)                                                                 \
   FP8_INST(D, SB, CA, kExpExact, false) FP8_INST(D, SB, CA, kExpSchraudolph, false)           \
-  FP8_INST(D, SB, CA, kExpExact, true) FP8_INST(D, SB, CA, kExpSchraudolph, true)
+  FP8_INST(D, SB, CA, kExpExact, true) FP8_INST(D, SB, CA, kExpSchraudolph, true)             \
+  template __global__ void attn_fp8_kernel<D, SB, CA, kExpExact, true, 32>(AttnFp8Params);    \
+  template __global__ void attn_fp8_kernel<D, SB, CA, kExpSchraudolph, true, 32>(AttnFp8Params);
 FP8_INST_E(64, 64, false)
 FP8_INST_E(64, 64, true)
 FP8_INST_E(64, 128, false)
@@ -517,24 +564,33 @@ FP8_INST_E(128, 128, false)
 FP8_INST_E(128, 128, true)
 
 template <int D, int SB, int E, bool MX, class P>
-static void launch_dcem(const P& p, int causal, dim3 grid, hipStream_t stream) {
+static void launch_dcem(const P& p, int causal, int grp, dim3 grid, hipStream_t stream) {
   if constexpr (std::is_same<P, AttnFp8Params>::value) {
-    if (causal) attn_fp8_kernel<D, SB, true, E, MX><<<grid, 256, 0, stream>>>(p);
-    else attn_fp8_kernel<D, SB, false, E, MX><<<grid, 256, 0, stream>>>(p);
+    if (MX && grp == 32) {
+      if (causal) attn_fp8_kernel<D, SB, true, E, true, 32><<<grid, 256, 0, stream>>>(p);
+      else attn_fp8_kernel<D, SB, false, E, true, 32><<<grid, 256, 0, stream>>>(p);
+    } else if (causal) {
+      attn_fp8_kernel<D, SB, true, E, MX><<<grid, 256, 0, stream>>>(p);
+    } else {
+      attn_fp8_kernel<D, SB, false, E, MX><<<grid, 256, 0, stream>>>(p);
+    }
   } else {
     if (causal) attn_fp8_varlen_kernel<D, SB, true, E, MX><<<grid, 256, 0, stream>>>(p);
     else attn_fp8_varlen_kernel<D, SB, false, E, MX><<<grid, 256, 0, stream>>>(p);
   }
 }
 
+// mx: 0 scales folded into the score scale (V's on the matrix core), 1
+// power-of-two block scales on the matrix core, 2 the same per 32 channels
 template <int D, int SB, class P>
 static void launch_dc(const P& p, int causal, int exp_mode, int mx, dim3 grid, hipStream_t stream) {
+  const int grp = mx == 2 ? 32 : 0;
   if (exp_mode == kExpSchraudolph) {
-    if (mx) launch_dcem<D, SB, kExpSchraudolph, true>(p, causal, grid, stream);
-    else launch_dcem<D, SB, kExpSchraudolph, false>(p, causal, grid, stream);
+    if (mx) launch_dcem<D, SB, kExpSchraudolph, true>(p, causal, grp, grid, stream);
+    else launch_dcem<D, SB, kExpSchraudolph, false>(p, causal, grp, grid, stream);
   } else {
-    if (mx) launch_dcem<D, SB, kExpExact, true>(p, causal, grid, stream);
-    else launch_dcem<D, SB, kExpExact, false>(p, causal, grid, stream);
+    if (mx) launch_dcem<D, SB, kExpExact, true>(p, causal, grp, grid, stream);
+    else launch_dcem<D, SB, kExpExact, false>(p, causal, grp, grid, stream);
   }
 }
 

@@ -127,7 +127,7 @@ extern "C" {
 int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v, int B, int H, int N, int D,
                           int scale_block, int hadamard, uint64_t seed, unsigned flags, uint8_t* q8, uint8_t* k8,
                           uint8_t* v8, float* q_descale, float* k_descale, float* v_descale, void* stream) {
-  if (flags & ~(unsigned)ATTN_FP8_MX) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(unsigned)(ATTN_FP8_MX | ATTN_FP8_MX32)) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
   CHECK(check_sizes(B, H, N, D));
   CHECK(check_sb(scale_block));
   CHECK(check_ptr(q, 16, "q"));
@@ -139,8 +139,8 @@ int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v, int B,
   CHECK(check_ptr(q_descale, 4, "q_descale"));
   CHECK(check_ptr(k_descale, 4, "k_descale"));
   CHECK(check_ptr(v_descale, 4, "v_descale"));
-  if ((long long)B * H * ((N + scale_block - 1) / scale_block) >= (1LL << 31))
-    return fail(ATTN_EINVAL, "B * H * ceil(N / scale_block) must be < 2^31");
+  if ((long long)B * H * ((N + scale_block - 1) / scale_block) * ((flags & ATTN_FP8_MX32) ? D / 32 : 1) >= (1LL << 31))
+    return fail(ATTN_EINVAL, "the descale count must be < 2^31");
   CHECK(check_device());
   attnfp8::QuantParams p;
   p.q = q; p.k = k; p.v = v;
@@ -151,7 +151,8 @@ int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v, int B,
   p.hadamard = hadamard ? 1 : 0;
   p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
   p.key1 = (uint32_t)(seed >> 32);
-  return launched(attnfp8::launch_quantize(p, D, scale_block, (flags & ATTN_FP8_MX) ? 1 : 0, B * H,
+  const int pow2 = (flags & ATTN_FP8_MX32) ? 2 : ((flags & ATTN_FP8_MX) ? 1 : 0);
+  return launched(attnfp8::launch_quantize(p, D, scale_block, pow2, B * H,
                                            (hipStream_t)stream),
                   "quantize_qkv_fp8");
 }
@@ -166,7 +167,8 @@ int quantize_qkv_fp8(const float* q, const float* k, const float* v, int B, int 
 int attn_fp8_fwd_opts(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_descale,
                       const float* k_descale, const float* v_descale, int B, int H, int N, int D, int scale_block,
                       int hadamard, int causal, unsigned flags, uint16_t* o_bf16, float* lse, void* stream) {
-  if (flags & ~(unsigned)(ATTN_FP8_EXP2_SCHRAUDOLPH | ATTN_FP8_MX)) return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(unsigned)(ATTN_FP8_EXP2_SCHRAUDOLPH | ATTN_FP8_MX | ATTN_FP8_MX32))
+    return fail(ATTN_EINVAL, "unknown flags 0x%x", flags);
   CHECK(check_sizes(B, H, N, D));
   CHECK(check_sb(scale_block));
   CHECK(check_ptr(q8, 16, "q8"));
@@ -189,7 +191,7 @@ int attn_fp8_fwd_opts(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, c
   if (hadamard) sc /= D;
   p.score_scale = (float)sc;
   const int exp_mode = (flags & ATTN_FP8_EXP2_SCHRAUDOLPH) ? 1 : 0;
-  const int mx = (flags & ATTN_FP8_MX) ? 1 : 0;
+  const int mx = (flags & ATTN_FP8_MX32) ? 2 : ((flags & ATTN_FP8_MX) ? 1 : 0);
   return launched(attnfp8::launch_attn_fp8(p, D, scale_block, causal ? 1 : 0, exp_mode, mx, B * H,
                                            (hipStream_t)stream),
                   "attn_fp8_fwd");

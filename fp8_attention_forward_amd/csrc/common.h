@@ -2,9 +2,13 @@
 //
 // Lane layouts used below (CDNA4 MFMA, wave64):
 //   * v_mfma_f32_32x32x64_f8f6f4 (fp8 e4m3 operands): lane l holds, for the A
-//     operand, row (l % 32) and the 32 k-values 32*(l/32) .. +31 (one byte
-//     each); the B operand likewise with column (l % 32).  The accumulator
-//     register r of lane l is element (row 8*(r/4) + 4*(l/32) + r%4, col l%32).
+//     operand, row (l % 32) and 32 k-values in two 16-byte halves: bytes
+//     0..15 are k = 16*(l/32) + 0..15, bytes 16..31 are k = 32 + 16*(l/32) +
+//     0..15 (measured on the device with per-lane E8M0 scales: the 32-element
+//     scale block k = 0..31 is the first half of both lane halves); the B
+//     operand likewise with column (l % 32).  The accumulator register r of
+//     lane l is element (row 8*(r/4) + 4*(l/32) + r%4, col l%32).  The scale
+//     operand of lane l applies to row (column) l % 32 and k-block l / 32.
 //   * v_mfma_f32_32x32x16_bf16: the same with 8 bf16 k-values per lane,
 //     k = 8*(l/32) .. +7.
 //   * ds_read_b64_tr_b8: within each group of 16 lanes, lane i names an 8-byte

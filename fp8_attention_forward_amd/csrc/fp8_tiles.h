@@ -58,6 +58,12 @@ struct ExpArgs {
 };
 constexpr int kBC = kFp8KeyTile; // keys per tile
 
+// First channel of the 16-byte operand piece `half` that lane half h feeds to
+// K-step ks of the score product: channel = the matrix core's k index (plus
+// 64 ks), so each 32-channel group is one 32-element scale block of the
+// scaled MFMA (lane half h = l / 32).
+__device__ __forceinline__ constexpr int op_channel(int ks, int h, int half) { return 64 * ks + 32 * half + 16 * h; }
+
 template <int D>
 struct Fp8Cfg {
   static constexpr int KSTEPS = D / 64;      // K-steps of the QK^T contraction
@@ -92,7 +98,7 @@ __device__ __forceinline__ int swz_v(int row) {
 template <int D>
 struct Fp8LaneOffsets {
   using C = Fp8Cfg<D>;
-  int k[C::KSTEPS][2];   // K row (lane % 32), 16-byte halves of k-step ks; + sub * 32 * D
+  int k[C::KSTEPS][2];   // K row (lane % 32), its two 16-byte pieces of k-step ks; + sub * 32 * D
   int v[C::NDT];         // V^T source row for d-tile dt; + 16 rr * D
 
   __device__ __forceinline__ explicit Fp8LaneOffsets(int lane) {
@@ -101,7 +107,7 @@ struct Fp8LaneOffsets {
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) k[ks][half] = ql * D + 16 * ((4 * ks + 2 * h + half) ^ swz_k<D>(ql));
+      for (int half = 0; half < 2; ++half) k[ks][half] = ql * D + 16 * ((op_channel(ks, h, half) / 16) ^ swz_k<D>(ql));
     // ds_read_b64_tr_b8 source lane i of 16-lane group g supplies key byte t = i / 2 of
     // the (8 rr + t)-th operand byte; that key is row 8 (j / 4) + 4 h + j % 4, j = 8 rr + t
     const int g = lane >> 4;
@@ -146,16 +152,24 @@ __device__ __forceinline__ v16f mfma_f8x(const v8i& a, const v8i& b, const v16f&
 // E8M0 exponent of a power-of-two float (2^-127 is the subnormal 0x00400000)
 __device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__builtin_bit_cast(uint32_t, pow2) >> 23) & 0xFF; }
 
+// E8M0 scale operands of the score product, one per K-step of the
+// contraction (lane half h of K-step ks covers channels 64 ks + 32 h ..
+// + 31: with 32-channel scales they differ per lane half and per K-step)
+template <int D>
+struct KsScales {
+  int v[Fp8Cfg<D>::KSTEPS];
+};
+
 template <int D, bool MX>
-__device__ __forceinline__ v16f qk_mfma(const KOps<D>& k, const v8i (&qop)[Fp8Cfg<D>::KSTEPS], int sub, int sk,
-                                        int sq) {
+__device__ __forceinline__ v16f qk_mfma(const KOps<D>& k, const v8i (&qop)[Fp8Cfg<D>::KSTEPS], int sub,
+                                        const KsScales<D>& sk, const KsScales<D>& sq) {
   v16f acc = {};
 #pragma unroll
   for (int ks = 0; ks < Fp8Cfg<D>::KSTEPS; ++ks) {
     const v4i& a0 = k.r[sub][ks][0];
     const v4i& a1 = k.r[sub][ks][1];
     v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    acc = mfma_f8x<MX>(a, qop[ks], acc, sk, sq);
+    acc = mfma_f8x<MX>(a, qop[ks], acc, sk.v[ks], sq.v[ks]);
   }
   return acc;
 }

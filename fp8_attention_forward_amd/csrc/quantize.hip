@@ -75,9 +75,11 @@ __device__ __forceinline__ float exp2i(int e) {
 }
 
 // One scale block: rows [0, nrows) (nrows <= SB) of src, D floats each ->
-// e4m3 codes at dst (same row layout) and the block's descale at *dsc.
+// e4m3 codes at dst (same row layout) and the block's descale at *dsc, or,
+// with GRP = 32, one power-of-two descale per 32 channels at dsc[0 .. D/32)
+// (the MX block of 32 elements; pow2 must then be set).
 // Called by every thread of the workgroup (it holds a workgroup barrier).
-template <int D, int SB>
+template <int D, int SB, int GRP = 0>
 __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, int nrows, float* dsc, bool rotate,
                                                bool pow2, uint32_t key0, uint32_t key1) {
 #pragma clang fp contract(off)
@@ -139,11 +141,29 @@ __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, i
   for (int it = 0; it < ITERS; ++it)
 #pragma unroll
     for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(x[it][e]));
-  m = wave_max(m);
-  __shared__ float red[4];
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float a;
+  if constexpr (GRP == 0) {
+    m = wave_max(m);
+    __shared__ float red[4];
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  } else {
+    // the GRP / 4 lanes of a channel group in a row, then the rows of the
+    // wave (lanes LPR apart), then the four waves
+    static_assert(GRP == 32, "32-channel groups");
+    m = fmaxf(m, xor_lanes<1>(m));
+    m = fmaxf(m, xor_lanes<2>(m));
+    m = fmaxf(m, xor_lanes<4>(m));
+    if constexpr (LPR == 16) m = fmaxf(m, xor_lanes<16>(m));
+    m = fmaxf(m, swap_halves(m));
+    constexpr int NG = D / GRP;
+    __shared__ float redg[4][NG];
+    if (lane < LPR && (rlane & 7) == 0) redg[wave][rlane >> 3] = m;
+    __syncthreads();
+    const int g = rlane >> 3;
+    a = fmaxf(fmaxf(redg[0][g], redg[1][g]), fmaxf(redg[2][g], redg[3][g]));
+  }
   float inv, descale;
   if (pow2) {
     const int e = pow2_scale_exponent(a);
@@ -153,7 +173,11 @@ __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, i
     inv = a == 0.0f ? 1.0f : 448.0f / a;
     descale = a == 0.0f ? 1.0f : a / 448.0f;
   }
-  if (tid == 0) *dsc = descale;
+  if constexpr (GRP == 0) {
+    if (tid == 0) *dsc = descale;
+  } else {
+    if (tid < LPR && (rlane & 7) == 0) dsc[rlane >> 3] = descale;
+  }
 
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
@@ -168,7 +192,8 @@ __device__ __forceinline__ void quantize_block(const float* src, uint8_t* dst, i
 }
 
 // Dense layout: one workgroup per (block, batch*head) and tensor (blockIdx.y).
-template <int D, int SB, bool POW2>
+// GRP = 32: power-of-two descales per 32 channels, [..][nblk][D / 32].
+template <int D, int SB, bool POW2, int GRP = 0>
 __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
   const int blk = blockIdx.x % p.nblk;
   const int bh = blockIdx.x / p.nblk;
@@ -179,8 +204,9 @@ __global__ __launch_bounds__(256) void quantize_qkv_kernel(QuantParams p) {
   const int row0 = blk * SB;
   const size_t off = ((size_t)bh * p.N + row0) * D;
   const int nrows = p.N - row0 < SB ? p.N - row0 : SB;
-  quantize_block<D, SB>(src + off, dst + off, nrows, dsc + (size_t)bh * p.nblk + blk, p.hadamard && tensor < 2,
-                        POW2 || tensor == 2, p.key0, p.key1);
+  constexpr int NG = GRP == 0 ? 1 : D / GRP;
+  quantize_block<D, SB, GRP>(src + off, dst + off, nrows, dsc + ((size_t)bh * p.nblk + blk) * NG,
+                             p.hadamard && tensor < 2, POW2 || tensor == 2 || GRP != 0, p.key0, p.key1);
 }
 
 // Packed documents ("FLAMIA", Abstract and 4.1 Performance on Packed
@@ -237,6 +263,7 @@ __global__ __launch_bounds__(256) void quantize_qkv_varlen_kernel(QuantVarlenPar
 #define QUANT_INST(D, SB) \
   template __global__ void quantize_qkv_kernel<D, SB, false>(QuantParams); \
   template __global__ void quantize_qkv_kernel<D, SB, true>(QuantParams); \
+  template __global__ void quantize_qkv_kernel<D, SB, true, 32>(QuantParams); \
   template __global__ void quantize_qkv_varlen_kernel<D, SB, false>(QuantVarlenParams); \
   template __global__ void quantize_qkv_varlen_kernel<D, SB, true>(QuantVarlenParams);
 QUANT_INST(64, 64)
@@ -244,9 +271,12 @@ QUANT_INST(64, 128)
 QUANT_INST(128, 64)
 QUANT_INST(128, 128)
 
+// pow2: 0 amax / 448 for Q and K, 1 power-of-two block scales, 2 power-of-two
+// scales per 32 channels
 template <int D, int SB>
-static void launch_q(const QuantParams& p, bool pow2, dim3 grid, hipStream_t stream) {
-  if (pow2) quantize_qkv_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
+static void launch_q(const QuantParams& p, int pow2, dim3 grid, hipStream_t stream) {
+  if (pow2 == 2) quantize_qkv_kernel<D, SB, true, 32><<<grid, 256, 0, stream>>>(p);
+  else if (pow2) quantize_qkv_kernel<D, SB, true><<<grid, 256, 0, stream>>>(p);
   else quantize_qkv_kernel<D, SB, false><<<grid, 256, 0, stream>>>(p);
 }
 

@@ -94,10 +94,21 @@ int quantize_qkv_fp8(const float* q, const float* k, const float* v,
  *     Descales that are not powers of two give wrong results (only their
  *     exponent fields are read). */
 #define ATTN_FP8_MX 2u
+/* ATTN_FP8_MX32 -- the MX scales at their own granularity ("FLAMIA", 2
+ * Background: MX formats share one E8M0 scale per block of 32 elements; 4.2
+ * Numerical Accuracy evaluates per-32-element scaling): one power-of-two
+ * scale per (scale_block tokens x 32 channels) of Q, K and V, applied by the
+ * scaled FP8 MFMA per lane (the 32 channels one lane feeds to one product
+ * share a scale).  Descales are [B][H][ceil(N / scale_block)][D / 32]
+ * (float32 2^e, the smallest with the group's amax <= 448 * 2^e, e clamped to
+ * [-127, 127], 2^0 for an all-zero group), written by quantize_qkv_fp8_opts
+ * and read by attn_fp8_fwd_opts with this flag (alone or with
+ * ATTN_FP8_EXP2_SCHRAUDOLPH; ATTN_FP8_MX is implied).  Dense layout only. */
+#define ATTN_FP8_MX32 8u
 
 /* quantize_qkv_fp8_opts -- quantize_qkv_fp8 with option flags (quantize_qkv_fp8
- * is this call with flags = 0).  flags: ATTN_FP8_MX or 0; any other bit ->
- * ATTN_EINVAL. */
+ * is this call with flags = 0).  flags: ATTN_FP8_MX, ATTN_FP8_MX32 or 0; any
+ * other bit -> ATTN_EINVAL. */
 int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v,
                           int B, int H, int N, int D, int scale_block, int hadamard, uint64_t seed,
                           unsigned flags, uint8_t* q8, uint8_t* k8, uint8_t* v8,
@@ -128,8 +139,8 @@ int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
 
 /* attn_fp8_fwd_opts -- attn_fp8_fwd with option flags (attn_fp8_fwd is this
  * call with flags = 0).
- *   flags             : any combination of ATTN_FP8_MX (above) and
- *                       ATTN_FP8_EXP2_SCHRAUDOLPH.
+ *   flags             : any combination of ATTN_FP8_MX or ATTN_FP8_MX32
+ *                       (above) and ATTN_FP8_EXP2_SCHRAUDOLPH.
  *                       ATTN_FP8_EXP2_SCHRAUDOLPH -> the probabilities use
  *                       Schraudolph's bit-level exponential (N. N. Schraudolph,
  *                       "A fast, compact approximation of the exponential

@@ -29,7 +29,9 @@ Dequantised value: e4m3_value(code) * descale.
 
 Power-of-two (microscaling, E8M0) scales, the option ``pow2=True`` ([P3]
 FLAMIA, 2 Background: MX formats give each block of low-bit codes one shared
-scale, applied by block-scaled matrix units).  The pages do not fix how the
+scale, applied by block-scaled matrix units; the MX blocks there are 32
+elements, which ``group=32`` gives: one scale per scale_block tokens x 32
+channels).  The pages do not fix how the
 exponent is chosen; the reading taken is the power-of-two form of the scale
 above that never saturates: descale = 2^e with e the smallest integer such
 that a <= 448 * 2^e, clamped to the E8M0 range [-127, 127]; inv = 2^-e; a block
@@ -72,22 +74,29 @@ def pow2_exponent(a):
     return np.clip(e, -127, 127).astype(np.int64)
 
 
-def quantize_tensor(x, scale_block, signs=None, pow2=False):
-    """One tensor [..., N, d] -> (codes uint8 [..., N, d], descale float32 [..., nblk]).
+def quantize_tensor(x, scale_block, signs=None, pow2=False, group=None):
+    """One tensor [..., N, d] -> (codes uint8 [..., N, d], descale float32).
 
     ``signs`` (float32 +-1 of length d) turns the rotation on; None leaves x unrotated.
-    ``pow2`` selects the power-of-two (E8M0) block scales.
+    ``pow2`` selects the power-of-two (E8M0) block scales.  ``group`` (a divisor
+    of d, power-of-two scales only) gives every block one scale per ``group``
+    consecutive channels instead of one for all d: descale [..., nblk, d / group];
+    otherwise descale [..., nblk].
     """
     y = np.asarray(x, dtype=np.float32)
     if signs is not None:
         y = rotate(y, signs)
     n, d = y.shape[-2], y.shape[-1]
+    if group is not None and (not pow2 or d % group):
+        raise ValueError("channel groups need power-of-two scales and must divide d")
+    g = d if group is None else group
     nb = num_blocks(n, scale_block)
     lead = y.shape[:-2]
-    amax = np.empty(lead + (nb,), dtype=np.float32)
+    amax = np.empty(lead + (nb, d // g), dtype=np.float32)
     for blk in range(nb):
         rows = y[..., blk * scale_block:min(n, (blk + 1) * scale_block), :]
-        amax[..., blk] = np.abs(rows).max(axis=(-2, -1))
+        rows = rows.reshape(rows.shape[:-1] + (d // g, g))
+        amax[..., blk, :] = np.abs(rows).max(axis=(-3, -1))
     zero = amax == 0
     if pow2:
         e = pow2_exponent(amax)
@@ -97,30 +106,36 @@ def quantize_tensor(x, scale_block, signs=None, pow2=False):
         with np.errstate(divide="ignore", invalid="ignore"):
             inv = np.where(zero, np.float32(1.0), _F448 / amax).astype(np.float32)
             descale = np.where(zero, np.float32(1.0), amax / _F448).astype(np.float32)
-    inv_rows = np.repeat(inv, scale_block, axis=-1)[..., :n]
-    v = y * inv_rows[..., None]                 # float32 product, round to nearest even
-    return e4m3.encode(v), descale
+    inv_rows = np.repeat(inv, scale_block, axis=-2)[..., :n, :]          # [..., n, d / g]
+    v = y * np.repeat(inv_rows, g, axis=-1)     # float32 product, round to nearest even
+    return e4m3.encode(v), (descale if group is not None else descale[..., 0])
 
 
-def quantize_qkv(q, k, v, scale_block, hadamard, seed, pow2=False):
+def quantize_qkv(q, k, v, scale_block, hadamard, seed, pow2=False, group=None):
     """The full pre-processing of one attention call.
 
     Returns (q8, k8, v8, q_descale, k_descale, v_descale).  Q and K share one
     sign vector drawn from ``seed``; V is never rotated.  V's blocks always
     take power-of-two scales (the product with P applies them exactly);
-    ``pow2`` gives Q and K power-of-two scales too.
+    ``pow2`` gives Q and K power-of-two scales too; ``group`` (with pow2)
+    gives all three one scale per ``group`` channels of a block.
     """
     d = np.shape(q)[-1]
     signs = sign_vector(seed, d) if hadamard else None
-    q8, qd = quantize_tensor(q, scale_block, signs, pow2)
-    k8, kd = quantize_tensor(k, scale_block, signs, pow2)
-    v8, vd = quantize_tensor(v, scale_block, None, True)
+    q8, qd = quantize_tensor(q, scale_block, signs, pow2, group)
+    k8, kd = quantize_tensor(k, scale_block, signs, pow2, group)
+    v8, vd = quantize_tensor(v, scale_block, None, True, group)
     return q8, k8, v8, qd, kd, vd
 
 
 def dequantize(codes, descale, scale_block):
-    """float64 value of each code times its block's descale."""
+    """float64 value of each code times its block's descale (descale [..., nblk]
+    or, with channel groups, [..., nblk, d / group])."""
     vals = e4m3.decode(codes)
-    n = vals.shape[-2]
-    ds = np.repeat(np.asarray(descale, dtype=np.float64), scale_block, axis=-1)[..., :n]
+    n, d = vals.shape[-2], vals.shape[-1]
+    ds = np.asarray(descale, dtype=np.float64)
+    if ds.ndim == vals.ndim:                     # channel groups
+        ds = np.repeat(np.repeat(ds, scale_block, axis=-2)[..., :n, :], d // ds.shape[-1], axis=-1)
+        return vals * ds
+    ds = np.repeat(ds, scale_block, axis=-1)[..., :n]
     return vals * ds[..., None]

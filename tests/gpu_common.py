@@ -86,7 +86,7 @@ def check_fp8_vs_e1(o_gpu, lse_gpu, bars, tag=""):
 
 
 def check_heads_vs_e1(name, x_host, got_host, heads, scale_block, hadamard, causal, sign_seed, n_rows=4,
-                      exp2="exact", mx=False, workers=8):
+                      exp2="exact", mx=False, workers=8, group=None):
     """Full-size parity on whole heads: for every (b, h) in ``heads`` the
     oracle quantises that head (blocks never cross heads), the GPU codes and
     descales must equal it bit for bit, and O / LSE on sampled rows (always
@@ -105,7 +105,8 @@ def check_heads_vs_e1(name, x_host, got_host, heads, scale_block, hadamard, caus
     def one(bh):
         b, h = bh
         sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oq.quantize_qkv(q[sl], k[sl], v[sl], scale_block, hadamard, sign_seed, pow2=mx)
+        ref = oq.quantize_qkv(q[sl], k[sl], v[sl], scale_block, hadamard, sign_seed, pow2=mx or group is not None,
+                              group=group)
         for g, r, nm in zip(got_host[:6], ref, ("q8", "k8", "v8", "qd", "kd", "vd")):
             g = g[sl]
             same = np.array_equal(g, r) if r.dtype == np.uint8 else np.array_equal(g.view(np.uint32), r.view(np.uint32))

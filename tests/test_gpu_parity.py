@@ -164,6 +164,40 @@ def test_attn_fp8_mx_matches_e1(case):
     print(f"{case}: mx RMSE vs FP64 {rms(o - orf):.3e}")
 
 
+# One power-of-two scale per block x 32 channels (ATTN_FP8_MX32), the MX
+# block size: quantiser bit-exact, attention against E1 of those codes.
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}".format(*c[:6]))
+def test_quantize_mx32_bit_exact(case):
+    B, H, N, D, sb, had, seed, kind = case
+    q, k, v = workloads.generate(kind, B, H, N, D, 700 + N)
+    out = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=sb, hadamard=had, seed=seed, mx32=True)
+    torch.cuda.synchronize()
+    ref = oq.quantize_qkv(q, k, v, sb, had, seed, pow2=True, group=32)
+    for g, r, nm in zip((host(t) for t in out), ref, ("q8", "k8", "v8", "qd", "kd", "vd")):
+        assert g.shape == r.shape, nm
+        if r.dtype == np.uint8:
+            assert np.array_equal(g, r), f"{case} {nm}: {np.count_nonzero(g != r)} codes differ"
+        else:
+            assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), f"{case} {nm}"
+
+
+MX32_CASES = [c + ("exact",) for c in ATTN_CASES] + [c + ("schraudolph",) for c in ATTN_CASES[2:5]]
+
+
+@pytest.mark.parametrize("case", MX32_CASES, ids=lambda c: "B{}H{}N{}D{}sb{}had{}c{}-{}".format(*c[:7], c[8]))
+def test_attn_fp8_mx32_matches_e1(case):
+    B, H, N, D, sb, had, causal, kind, exp2 = case
+    q, k, v = workloads.generate(kind, B, H, N, D, 800 + N)
+    qq_gpu = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=sb, hadamard=had, seed=0x5EED, mx32=True)
+    o, lse = fa.attn_fp8_fwd(*qq_gpu, scale_block=sb, hadamard=had, causal=causal, exp2=exp2, mx32=True)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    qq = oq.quantize_qkv(q, k, v, sb, had, 0x5EED, pow2=True, group=32)
+    check_fp8_vs_e1(o, lse, oatt.emulated_fp8_attention_bars(*qq, sb, had, causal, exp2=exp2), tag=f"{case} mx32")
+    orf, _ = oatt.reference_attention(q, k, v, causal)
+    print(f"{case}: mx32 RMSE vs FP64 {rms(o - orf):.3e}")
+
+
 BF16_CASES = [
     (1, 2, 256, 64, False), (1, 2, 256, 64, True), (2, 2, 300, 128, False), (2, 2, 300, 128, True),
     (1, 1, 1, 128, True), (1, 2, 1000, 128, True), (1, 1, 65, 64, False),

@@ -35,10 +35,11 @@ def _some_heads(w, count=8):
     return sorted(hs)[:max(count, 2)]
 
 
-def _run(w, q, k, v, exp2="exact", mx=False):
+def _run(w, q, k, v, exp2="exact", mx=False, mx32=False):
     out = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=w.scale_block, hadamard=w.hadamard,
-                              seed=w.sign_seed, mx=mx)
-    o, lse = fa.attn_fp8_fwd(*out, scale_block=w.scale_block, hadamard=w.hadamard, causal=w.causal, exp2=exp2, mx=mx)
+                              seed=w.sign_seed, mx=mx, mx32=mx32)
+    o, lse = fa.attn_fp8_fwd(*out, scale_block=w.scale_block, hadamard=w.hadamard, causal=w.causal, exp2=exp2, mx=mx,
+                             mx32=mx32)
     torch.cuda.synchronize()
     return [host(t) for t in out] + [host(o), host(lse)]
 
@@ -77,6 +78,18 @@ def test_workload_fp8_options_parity(name, exp2, mx):
                             w.causal, w.sign_seed, exp2=exp2, mx=mx)
     r = np.array(res)
     print(f"[{name} {exp2} mx={mx}] RMSE vs E1 max {r[:, 0].max():.3e}, max err {r[:, 1].max():.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["outlier", "channel_norot"])
+def test_workload_fp8_mx32_parity(name):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.generate_workload(w)
+    print(f"\n[{name} mx32] quantise + attention on the GPU", flush=True)
+    got = _run(w, q, k, v, mx32=True)
+    res = check_heads_vs_e1(f"{name} mx32", (q, k, v), got, _some_heads(w), w.scale_block, w.hadamard, w.causal,
+                            w.sign_seed, group=32)
+    r = np.array(res)
+    print(f"[{name} mx32] RMSE vs E1 max {r[:, 0].max():.3e}, max err {r[:, 1].max():.3e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["outlier", "outlier_causal", "ablation_tail"])

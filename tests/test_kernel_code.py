@@ -63,8 +63,10 @@ def _resources(src, names):
 @pytest.fixture(scope="module")
 def kernels():
     funcs = _compile(SRC, "15attn_fp8_kernel|22attn_fp8_varlen_kernel")
-    # (dense, packed) x D x scale block x causal x exponential mode x MX
-    assert len(funcs) == 64, sorted(funcs)
+    # (dense, packed) x D x scale block x causal x exponential mode x MX, plus
+    # the dense kernels with 32-channel MX scales (D x scale block x causal x
+    # exponential mode)
+    assert len(funcs) == 80, sorted(funcs)
     return funcs
 
 
