@@ -48,6 +48,9 @@ def parse():
                     help="skip the causal, ablation-shape and channel-outlier configurations")
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode workloads (for profiling); --copy-mb adds a calibration copy")
+    ap.add_argument("--decode-split", type=int, default=0,
+                    help="decode key ranges: 0 = the library's choice (balanced shares), >0 = fixed ranges of that "
+                         "many keys per wave")
     ap.add_argument("--attn-only", action="store_true", help="time only attn_fp8_fwd launches (for profiling)")
     ap.add_argument("--bf16", action="store_true", help="with --attn-only: time the BF16 twin's launches instead")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -452,8 +455,26 @@ def config_accuracy(configs, samples):
 DECODE_NAMES = ("decode_gqa", "decode_gqa_spec")
 
 
+def decode_partials(w, L, split, waves=2048):
+    """Partials one decode call writes (and the merge reads back): fixed ranges,
+    one per four ranges of each (sequence, K/V head) that holds keys; balanced
+    shares, one per piece, i.e. per interval between consecutive share and
+    segment boundaries of the flat tile order (64-key tiles, sequence-major,
+    then K/V head)."""
+    import numpy as np
+    if split:
+        return int(w.Hkv * (-(-L // (4 * split))).sum())
+    nt = -(-L // 64)
+    T = int(w.Hkv * nt.sum())
+    W = min(waves, -(-min(waves, w.B * w.Hkv * -(-w.Ncap // 64)) // 4) * 4, T)
+    cuts = {T * i // W for i in range(1, W)}
+    seg = np.cumsum(np.repeat(nt, w.Hkv))
+    cuts |= {int(x) for x in seg[:-1] if 0 < x < T}
+    return len(cuts) + 1
+
+
 def decode_leg(args, fa, workloads, torch, dev, stream):
-    """Decode against an FP8 K/V cache: attn_fp8_decode (split kernel + merge)
+    """Decode against an FP8 K/V cache: attn_fp8_decode (range kernel + merge)
     with the cache and the new queries already quantised and resident in HBM.
     HBM-bound: reported as the K/V cache bytes read per second and as all
     algorithmic bytes (cache codes and descales, queries, partials written and
@@ -470,15 +491,15 @@ def decode_leg(args, fa, workloads, torch, dev, stream):
         del q, k, v
         sl_np = w.seqlens()
         sl = torch.from_numpy(sl_np).to(dev)
-        split = fa.attn_fp8_decode_split(w.B, w.Hkv, w.Ncap, 0)
-        ws = torch.empty(fa.attn_fp8_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Ncap, w.D, 0),
+        split = fa.attn_fp8_decode_split(w.B, w.Hkv, w.Ncap, args.decode_split)
+        ws = torch.empty(fa.attn_fp8_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Ncap, w.D, args.decode_split),
                          dtype=torch.uint8, device=dev)
         o = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
 
         def call():
             fa.attn_fp8_decode(q8, qd, k8, v8, kd, vd, sl, scale_block=w.scale_block, hadamard=w.hadamard,
-                               causal=w.causal, out=(o, lse), workspace=ws)
+                               causal=w.causal, split=args.decode_split, out=(o, lse), workspace=ws)
 
         for _ in range(5):
             call()
@@ -493,14 +514,13 @@ def decode_leg(args, fa, workloads, torch, dev, stream):
         ms = a.elapsed_time(b) / n
         L = sl_np.astype(np.int64)
         kv = w.kv_bytes()
-        nsplit = -(-w.Ncap // (4 * split))
         mq = (w.Hq // w.Hkv) * w.Sq
         total = (kv + 2 * 4 * w.Hkv * int((-(-L // w.scale_block)).sum()) + w.B * w.Hq * w.Sq * (w.D + 4)
-                 + 2 * w.B * w.Hkv * nsplit * mq * (w.D + 2) * 4 + w.B * w.Hq * w.Sq * (2 * w.D + 4))
+                 + 2 * decode_partials(w, L, split) * mq * (w.D + 2) * 4 + w.B * w.Hq * w.Sq * (2 * w.D + 4))
         out[name] = {
             "workload": f"B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} D{w.D} cache {w.Ncap}, lengths "
                         f"{int(L.min())}..{int(L.max())} (mean {int(L.mean())}), scale block {w.scale_block}",
-            "us": round(ms * 1e3, 2), "split": split,
+            "us": round(ms * 1e3, 2), "schedule": f"fixed ranges of {split} keys" if split else "balanced shares",
             "kv_cache_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
             "algorithmic_gbs": round(total / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -339,13 +339,12 @@ __global__ __launch_bounds__(256, 3) void attn_bf16_kernel(AttnBf16Params p) {
 #undef BF16_STEP
 
   // Tail: diagonal and ragged tiles, waves that stop early; run-time slots and
-  // full waits (vmcnt(0)): at D = 128 the causal instance reloads a spilled
-  // register in this loop, a vector-memory operation that a partial count of
-  // the tile loads would not include.
+  // the main loop's partial wait (every step issues the same loads, so the
+  // count still names the previous step's).
   for (; t < n_kt_wg; ++t) {
     const bool active = t <= kt_w;
     if (active) bf16_phaseA<D>(s, st, c);
-    wait_vmem_all();
+    wait_vmem_prev_step<2 * C::CPW>();
     workgroup_barrier();
     issue_tile16<D, false>(kh, lim, t + 3, KS + (t % kBf16Ring) * C::TILE, ln);
     issue_tile16<D, true>(vh, lim, t + 2, VS + ((t + 2) % kBf16Ring) * C::TILE, ln);
@@ -356,6 +355,9 @@ __global__ __launch_bounds__(256, 3) void attn_bf16_kernel(AttnBf16Params p) {
   wait_vmem_all();   // no tile load may still be writing LDS when the workgroup ends
 
   // ---- epilogue: O = O_acc / l ; LSE = ln 2 * (m + log2 l)
+  // (the lane's half is recomputed here rather than kept live through the
+  // tail, which runs at the register limit of three waves per SIMD)
+  const int h_out = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
   const float l_tot = st.l_acc + swap_halves(st.l_acc);
   const float inv_l = 1.0f / l_tot;
   if (my_q < N) {
@@ -364,12 +366,12 @@ __global__ __launch_bounds__(256, 3) void attn_bf16_kernel(AttnBf16Params p) {
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int d = 32 * dt + 8 * a + 4 * h;
+        const int d = 32 * dt + 8 * a + 4 * h_out;
         uint32_t w0 = pk_bf16(st.o[dt][4 * a + 0] * inv_l, st.o[dt][4 * a + 1] * inv_l);
         uint32_t w1 = pk_bf16(st.o[dt][4 * a + 2] * inv_l, st.o[dt][4 * a + 3] * inv_l);
         *(v2i*)(orow + d) = (v2i){(int)w0, (int)w1};
       }
-    if (h == 0) p.lse[(size_t)bh * N + my_q] = kLn2 * (st.m_ref + __builtin_amdgcn_logf(l_tot));
+    if (h_out == 0) p.lse[(size_t)bh * N + my_q] = kLn2 * (st.m_ref + __builtin_amdgcn_logf(l_tot));
   }
 }
 

@@ -40,33 +40,26 @@
 
 namespace attnfp8 {
 
+// The running-softmax loop of one wave over the keys [k0, k1) of sequence b
+// (length L) and K/V head hk, for all MQ query rows: O unnormalised, the
+// reference maximum m and this lane's half of the row sum l.  vbuf0: the
+// wave's two V tile buffers in LDS.
+template <int D>
+struct DecodeState {
+  v16f o[Fp8Cfg<D>::NDT];
+  float m_ref;
+  float l_acc;
+};
+
 template <int D, int SB, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_range(const DecodeParams& p, int b, int hk, int L, int k0, int k1,
+                                             uint8_t* vbuf0, DecodeState<D>& st) {
   using C = Fp8Cfg<D>;
   static_assert(SB % kBC == 0, "a key tile lies in one scale block");
-  // two V buffers per wave during the loop, the merge after it (dynamic
-  // size: decode_lds_bytes)
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
   const int ql = lane & 31;
   const int h = lane >> 5;
-  // (the split index is the slow grid dimension: every sequence's first
-  // splits are dispatched before any later ones, so the splits past the
-  // shorter sequences' ends come last and leave while the others finish)
-  const int bk = blockIdx.x;                   // batch * Hkv + K/V head
-  const int xs = blockIdx.y;                   // split
-  const int b = bk / p.Hkv;
-  const int hk = bk - b * p.Hkv;
-  int L = p.seqlens[b];
-  L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
-  // splits past the sequence's end hold no key: nothing to write (the merge
-  // reads only the splits below ceil(L / (4 split)))
-  if (xs * kWaves * p.split >= L) return;
-  const int k0 = (xs * kWaves + wave) * p.split;
-  const int k1 = L < k0 + p.split ? L : k0 + p.split;
+  const int bk = b * p.Hkv + hk;
 
   // this lane's query row: r = g * Sq + i (query head hk * G + g, new token i)
   const int r = ql < p.MQ ? ql : 0;
@@ -88,7 +81,6 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
   const cfloat* kd = (const cfloat*)(p.kd + (size_t)bk * p.nblk);
   const cfloat* vd = (const cfloat*)(p.vd + (size_t)bk * p.nblk);   // (scalar loads in the loop)
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8 + kvh), 0, L * D, 0x00020000);
-  const uint8_t* vbuf0 = smem + wave * 2 * C::TILE;       // this wave's two V buffers
   const uint32_t vlds = lds_addr_of(vbuf0);
   const v4i rsv = make_rsrc(p.v8 + kvh, (uint32_t)(L * D));
   // buffer offset of the 16 bytes lane l moves into LDS chunk j: LDS (row,
@@ -119,18 +111,16 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
 #pragma unroll
     for (int j = 0; j < C::CHUNKS; ++j) buffer_to_lds16(rsv, t * D + voff[j], vlds + buf * C::TILE + j * 1024);
   };
-  // the first tile's loads go out before the descale maximum is formed
   if (k0 < k1) {
     load_k(k0);
     load_v(k0, 0);
   }
 
   const Fp8LaneOffsets<D> lo(lane);
-  v16f o[C::NDT];
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt) o[dt] = (v16f){};
-  float m_ref = -1e30f;
-  float l_acc = 0.0f;
+  for (int dt = 0; dt < C::NDT; ++dt) st.o[dt] = (v16f){};
+  st.m_ref = -1e30f;
+  st.l_acc = 0.0f;
   v8i pop = (v8i){};
 
   // Per tile t: one wait (tile t resident, and every transpose read of the
@@ -171,20 +161,20 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[sub][rr]);
     float tmax = mx * c;
     tmax = fmaxf(tmax, swap_halves(tmax));
-    const bool upd = tmax > m_ref + kTau;
-    const float m_new = upd ? tmax - kLift : m_ref;
-    const float alpha = upd ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-    m_ref = m_new;
+    const bool upd = tmax > st.m_ref + kTau;
+    const float m_new = upd ? tmax - kLift : st.m_ref;
+    const float alpha = upd ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
+    st.m_ref = m_new;
     if (__builtin_amdgcn_ballot_w64(upd)) {
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
+        for (int rr = 0; rr < 16; ++rr) st.o[dt][rr] *= alpha;
     }
     // P = 2^(t - m) in e4m3 (B operand of the P V product) and its row sum;
     // V's power-of-two block scale is applied inside the matrix core
     const int sv = e8m0_of(vd[blk]);
-    const ExpArgs<kExpExact> ex(c, -m_ref);
+    const ExpArgs<kExpExact> ex(c, -st.m_ref);
     float rs = 0.0f;
 #pragma unroll
     for (int sub = 0; sub < C::NSUB; ++sub)
@@ -199,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
         w = cvt_pk_fp8<true>(p2, p3, w);
         pop[4 * sub + a] = w;
       }
-    l_acc = alpha * l_acc + rs;
+    st.l_acc = alpha * st.l_acc + rs;
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
@@ -207,9 +197,42 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) part[rr] = lds_read_tr8(vcur + 16 * rr * D + lo.v[dt]);
       const v8i av = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
-      o[dt] = mfma_f8x<true>(av, pop, o[dt], sv, 127);
+      st.o[dt] = mfma_f8x<true>(av, pop, st.o[dt], sv, 127);
     }
   }
+}
+
+template <int D, int SB, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p) {
+  using C = Fp8Cfg<D>;
+  // two V buffers per wave during the loop, the merge after it (dynamic
+  // size: decode_lds_bytes)
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ql = lane & 31;
+  const int h = lane >> 5;
+  // (the split index is the slow grid dimension: every sequence's first
+  // splits are dispatched before any later ones, so the splits past the
+  // shorter sequences' ends come last and leave while the others finish)
+  const int bk = blockIdx.x;                   // batch * Hkv + K/V head
+  const int xs = blockIdx.y;                   // split
+  const int b = bk / p.Hkv;
+  const int hk = bk - b * p.Hkv;
+  int L = p.seqlens[b];
+  L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
+  // splits past the sequence's end hold no key: nothing to write (the merge
+  // reads only the splits below ceil(L / (4 split)))
+  if (xs * kWaves * p.split >= L) return;
+  const int k0 = (xs * kWaves + wave) * p.split;
+  const int k1 = L < k0 + p.split ? L : k0 + p.split;
+  DecodeState<D> st;
+  decode_range<D, SB, CAUSAL>(p, b, hk, L, k0, k1, smem + wave * 2 * C::TILE, st);
+  const float m_ref = st.m_ref;
+  const v16f (&o)[C::NDT] = st.o;
+  const float l_acc = st.l_acc;
 
   // ---- merge the four waves by their log-sum-exp: waves 1..3 write their
   // rows, scaled to the common maximum, into slabs of their own; wave 0 adds
@@ -266,6 +289,164 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_kernel(DecodeParams p)
   }
 }
 
+// Tiles of kBC keys per sequence over the batch (B <= 64 * kMaxSeqPerLane),
+// spread over the lanes of a wave: lane j holds sequences [per j, per j + per)
+// and the number of tiles of the sequences before them (one K/V head).  One
+// round of independent loads of the lengths, then a scan over the lanes.
+constexpr int kMaxSeqPerLane = 8;
+
+struct BatchTiles {
+  int per;
+  int nt[kMaxSeqPerLane];
+  int before;      // tiles of the sequences before this lane's
+  int total;       // tiles of the whole batch (one K/V head)
+
+  __device__ __forceinline__ BatchTiles(const int* seqlens, int B, int Ncap) {
+    const int lane = threadIdx.x & 63;
+    per = (B + 63) / 64;
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxSeqPerLane; ++i) {
+      const int b = lane * per + i;
+      int L = (i < per && b < B) ? seqlens[b] : 0;
+      L = L < 0 ? 0 : (L > Ncap ? Ncap : L);
+      nt[i] = (L + kBC - 1) / kBC;
+      sum += nt[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += u;
+    }
+    before = incl - sum;
+    total = __builtin_amdgcn_readlane(incl, 63);
+  }
+  // tiles of sequence b, and of the sequences before it (wave-uniform b)
+  __device__ __forceinline__ void of(int b, int& nt_b, int& before_b) const {
+    const int j = b / per;
+    int acc = __builtin_amdgcn_readlane(before, j);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxSeqPerLane; ++i) {
+      const int v = __builtin_amdgcn_readlane(nt[i], j);
+      if (i < b - j * per) acc += v;
+      if (i == b - j * per) n = v;
+    }
+    nt_b = n;
+    before_b = acc;
+  }
+  // the (sequence, K/V head, tile) of flat tile x < Hkv * total; the flat
+  // order is sequence, then K/V head, then tile
+  __device__ __forceinline__ void locate(long long x, int Hkv, int& b, int& hk, int& tile) const {
+    const unsigned long long mask = __builtin_amdgcn_ballot_w64((long long)Hkv * before <= x);
+    const int j = 63 - __builtin_clzll(mask);            // lane 0 always qualifies
+    long long rem = x - (long long)Hkv * __builtin_amdgcn_readlane(before, j);
+    long long frem = 0;
+    int fn = 1;
+    b = j * per;
+#pragma unroll
+    for (int i = 0; i < kMaxSeqPerLane; ++i) {
+      const int n = __builtin_amdgcn_readlane(nt[i], j);
+      const long long seg = (long long)Hkv * n;
+      if (rem >= 0 && i < per) {
+        if (rem < seg) {
+          b = j * per + i;
+          frem = rem;
+          fn = n;
+        }
+        rem -= seg;
+      }
+    }
+    hk = (int)(frem / fn);
+    tile = (int)(frem - (long long)hk * fn);
+  }
+};
+
+// The wave whose share of the flat tile range holds tile x (shares are
+// [floor(w T / W), floor((w + 1) T / W))): the largest w with
+// floor(w T / W) <= x, i.e. ceil((x + 1) W / T) - 1.
+__device__ __forceinline__ int wave_of_tile(long long x, long long T, int W) {
+  return (int)(((x + 1) * W + T - 1) / T) - 1;
+}
+
+// Partial (m, l, O unnormalised) of one wave's piece for the MQ rows.
+template <int D>
+__device__ __forceinline__ void write_partial(const DecodeParams& p, size_t slot, const DecodeState<D>& st) {
+  const int lane = threadIdx.x & 63;
+  const int ql = lane & 31;
+  const int h = lane >> 5;
+  const float l_tot = st.l_acc + swap_halves(st.l_acc);
+  if (ql < p.MQ) {
+    float* po = p.part_o + (slot * p.MQ + ql) * D;
+#pragma unroll
+    for (int dt = 0; dt < Fp8Cfg<D>::NDT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *(v4f*)(po + 32 * dt + 8 * a + 4 * h) =
+            (v4f){st.o[dt][4 * a + 0], st.o[dt][4 * a + 1], st.o[dt][4 * a + 2], st.o[dt][4 * a + 3]};
+    if (h == 0) {
+      p.part_m[slot * p.MQ + ql] = st.m_ref;
+      p.part_l[slot * p.MQ + ql] = l_tot;
+    }
+  }
+}
+
+// Balanced schedule: the tiles of every (sequence, K/V head) in one flat
+// order, cut into W equal shares, one per wave (W = 4 x the grid, or the
+// number of tiles T if that is smaller).  A share
+// may span several (sequence, K/V head) segments: each piece runs the loop on
+// its own and writes its partial to slot w + s (s = b Hkv + hk).  Along the
+// shares, w and s never decrease, so w + s is distinct for every piece and
+// the pieces of one segment sit in consecutive slots.
+template <int D, int SB, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fp8_decode_balanced_kernel(DecodeParams p) {
+  using C = Fp8Cfg<D>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = blockIdx.x * kWaves + wave;
+  const BatchTiles bt(p.seqlens, p.B, p.Ncap);
+  const long long T = (long long)p.Hkv * bt.total;
+  // (no more shares than tiles: every share then holds a tile, so the slots
+  // of a segment's pieces are consecutive with no unwritten one between)
+  const int W = T < p.nwave ? (int)T : p.nwave;
+  if (w >= W) return;
+  long long x = T * w / W;
+  const long long x1 = T * (w + 1) / W;
+  int b, hk, tile;
+  bt.locate(x, p.Hkv, b, hk, tile);
+  int nt, dummy;
+  bt.of(b, nt, dummy);
+  for (;;) {
+    // (all of it is wave-uniform; said so, so that the buffer descriptors
+    // built from it stay in scalar registers)
+    b = __builtin_amdgcn_readfirstlane(b);
+    hk = __builtin_amdgcn_readfirstlane(hk);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    int L = __builtin_amdgcn_readfirstlane(p.seqlens[b]);
+    L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
+    const long long left = x1 - x;
+    const int n = left < (long long)(nt - tile) ? (int)left : nt - tile;
+    const int k0 = tile * kBC;
+    const int k1 = L < (tile + n) * kBC ? L : (tile + n) * kBC;
+    DecodeState<D> st;
+    decode_range<D, SB, CAUSAL>(p, b, hk, L, k0, k1, smem + wave * 2 * C::TILE, st);
+    write_partial<D>(p, (size_t)w + (size_t)b * p.Hkv + hk, st);
+    x += n;
+    if (x >= x1) break;
+    // the next segment that holds a tile (one exists: x < x1 <= T)
+    tile = 0;
+    if (++hk == p.Hkv) {
+      hk = 0;
+      do {
+        if (++b >= p.B) return;
+        bt.of(b, nt, dummy);
+      } while (nt == 0);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
   constexpr int PER = D / 64;                        // channels per lane
@@ -279,10 +460,30 @@ __global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
   const int hk = bk - b * p.Hkv;
   const int g = r / p.Sq;
   const int i = r - g * p.Sq;
-  const size_t base = (size_t)bk * p.nsplit;
-  int L = p.seqlens[b];
-  L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
-  const int nx = (L + kWaves * p.split - 1) / (kWaves * p.split);   // splits that hold keys
+  size_t base;
+  int nx;                                            // partials that hold keys
+  if (p.nwave > 0) {
+    // balanced schedule: the waves whose shares meet this segment's tiles
+    const BatchTiles bt(p.seqlens, p.B, p.Ncap);
+    int nt_b, before_b;
+    bt.of(b, nt_b, before_b);
+    const long long T = (long long)p.Hkv * bt.total;
+    const long long x0 = (long long)p.Hkv * before_b + (long long)hk * nt_b;
+    nx = 0;
+    base = 0;
+    if (nt_b > 0) {
+      const int W = T < p.nwave ? (int)T : p.nwave;
+      const int wf = wave_of_tile(x0, T, W);
+      const int wl = wave_of_tile(x0 + nt_b - 1, T, W);
+      base = (size_t)wf + bk;
+      nx = wl - wf + 1;
+    }
+  } else {
+    base = (size_t)bk * p.nsplit;
+    int L = p.seqlens[b];
+    L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
+    nx = (L + kWaves * p.split - 1) / (kWaves * p.split);
+  }
   // the splits' maxima, one split per lane
   float M = -INFINITY;
   for (int x = lane; x < nx; x += 64) M = fmaxf(M, p.part_m[(base + x) * p.MQ + r]);
@@ -344,6 +545,13 @@ static size_t decode_lds_bytes(int D, int MQ) {
 
 template <int D, int SB>
 static void launch_dec(const DecodeParams& p, int causal, hipStream_t stream) {
+  if (p.nwave > 0) {
+    const dim3 grid(p.nwave / kWaves);
+    const size_t lds = (size_t)2 * kWaves * kBC * D;   // the waves' V buffers
+    if (causal) attn_fp8_decode_balanced_kernel<D, SB, true><<<grid, 256, lds, stream>>>(p);
+    else attn_fp8_decode_balanced_kernel<D, SB, false><<<grid, 256, lds, stream>>>(p);
+    return;
+  }
   dim3 grid(p.B * p.Hkv, p.nsplit);
   const size_t lds = decode_lds_bytes(D, p.MQ);
   if (causal) attn_fp8_decode_kernel<D, SB, true><<<grid, 256, lds, stream>>>(p);

@@ -101,8 +101,9 @@ struct DecodeParams {
   int MQ;          // G * Sq <= 32 query rows per K/V head
   int Ncap;
   int nblk;        // ceil(Ncap / scale_block)
-  int split;       // keys per wave range (multiple of 64)
-  int nsplit;      // ceil(Ncap / (4 * split)) partials per (batch, K/V head)
+  int split;       // fixed ranges: keys per wave range (multiple of 64)
+  int nsplit;      // fixed ranges: ceil(Ncap / (4 * split)) partials per (batch, K/V head)
+  int nwave;       // balanced schedule: waves sharing the tiles (0: fixed ranges)
   float score_scale;
 };
 

@@ -314,6 +314,21 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                   "attn_fp8_fwd_varlen");
 }
 
+// Balanced schedule of the decode (split 0, B <= 512): the number of waves
+// that share the batch's tiles: two workgroups of four waves on each of 256
+// compute units, fewer when the cache holds fewer tiles; 0 = fixed ranges.
+constexpr int kDecodeWaves = 2048;
+constexpr int kDecodeBalancedMaxB = 512;
+
+static int decode_waves(int B, int Hkv, int Ncap, int split) {
+  if (split != 0 || B > kDecodeBalancedMaxB) return 0;
+  const long long tmax = (long long)B * Hkv * ((Ncap + 63) / 64);
+  const long long w = tmax < kDecodeWaves ? tmax : kDecodeWaves;
+  return (int)((w + 3) / 4 * 4);
+}
+
+// Keys per range of the fixed-range schedule (split > 0, or B above the
+// balanced schedule's limit).
 static int decode_split(int B, int Hkv, int Ncap, int split) {
   if (split > 0) return split;
   // the largest power of two in [64, 1024] keys per wave that still gives
@@ -331,9 +346,11 @@ static int decode_split(int B, int Hkv, int Ncap, int split) {
 
 size_t attn_fp8_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Ncap, int D, int split) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Ncap < 1 || D < 1 || split < 0 || Hq % Hkv) return 0;
+  const long long mq = (long long)(Hq / Hkv) * Sq;
+  const int nw = decode_waves(B, Hkv, Ncap, split);
+  if (nw > 0) return (size_t)(((long long)nw + (long long)B * Hkv) * mq * (D + 2) * 4);
   const int s = decode_split(B, Hkv, Ncap, split);
   const long long nsplit = (Ncap + 4LL * s - 1) / (4LL * s);
-  const long long mq = (long long)(Hq / Hkv) * Sq;
   return (size_t)((long long)B * Hkv * nsplit * mq * (D + 2) * 4);
 }
 
@@ -354,7 +371,8 @@ static int decode_impl(const uint8_t* q8, const float* q_descale, const uint8_t*
   if ((long long)Ncap * D >= (1LL << 30)) return fail(ATTN_EINVAL, "Ncap * D must be < 2^30");
   if ((long long)B * Hkv > 65535) return fail(ATTN_EINVAL, "B * Hkv must be <= 65535");
   if (split < 0 || split % 64 || split > 8192) return fail(ATTN_EINVAL, "split must be 0 or a multiple of 64 up to 8192");
-  if ((Ncap + 4LL * decode_split(B, Hkv, Ncap, split) - 1) / (4LL * decode_split(B, Hkv, Ncap, split)) > 65535)
+  if (decode_waves(B, Hkv, Ncap, split) == 0 &&
+      (Ncap + 4LL * decode_split(B, Hkv, Ncap, split) - 1) / (4LL * decode_split(B, Hkv, Ncap, split)) > 65535)
     return fail(ATTN_EINVAL, "ceil(Ncap / (4 * split)) must be <= 65535");
   if ((long long)B * Hq * Sq >= (1LL << 31)) return fail(ATTN_EINVAL, "B * Hq * Sq must be < 2^31");
   CHECK(check_ptr(q8, 16, "q8"));
@@ -384,9 +402,11 @@ static int decode_impl(const uint8_t* q8, const float* q_descale, const uint8_t*
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.Sq = Sq; p.MQ = p.G * Sq;
   p.Ncap = Ncap;
   p.nblk = (Ncap + scale_block - 1) / scale_block;
+  p.nwave = decode_waves(B, Hkv, Ncap, split);
   p.split = decode_split(B, Hkv, Ncap, split);
   p.nsplit = (Ncap + 4 * p.split - 1) / (4 * p.split);
-  const size_t nparts = (size_t)B * Hkv * p.nsplit * p.MQ;
+  const size_t nparts =
+      (p.nwave > 0 ? (size_t)p.nwave + (size_t)B * Hkv : (size_t)B * Hkv * p.nsplit) * (size_t)p.MQ;
   p.part_o = (float*)workspace;
   p.part_m = p.part_o + nparts * D;
   p.part_l = p.part_m + nparts;
@@ -418,6 +438,7 @@ int attn_fp8_decode_noalloc(const uint8_t* q8, const float* q_descale, const uin
 
 int attn_fp8_decode_split(int B, int Hkv, int Ncap, int split) {
   if (B < 1 || Hkv < 1 || Ncap < 1 || split < 0) return 0;
+  if (decode_waves(B, Hkv, Ncap, split) > 0) return 0;
   return decode_split(B, Hkv, Ncap, split);
 }
 

@@ -264,30 +264,43 @@ int attn_fp8_fwd_varlen(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  * Query i of sequence b sits at position L_b - Sq + i; causal: it sees keys
  * up to that position.  Outputs o_bf16 [B][Hq][Sq][D], lse [B][Hq][Sq].
  *
- * The keys of a sequence are split into ranges of `split` keys (a multiple
- * of 64; 0 = the library's choice, attn_fp8_decode_split); each range runs
- * the loop of attn_fp8_fwd (P's V factor relative to the largest V descale
- * of the range) and the ranges merge by their log-sum-exp.
+ * The keys are cut into ranges; each range runs the loop of attn_fp8_fwd
+ * (64-key tiles, lazy reference, P in e4m3, V's power-of-two block scale
+ * inside the matrix core) and the ranges of one (sequence, K/V head) merge by
+ * their log-sum-exp.  Two schedules:
+ *   split = 0, B <= 512 (balanced shares): the 64-key tiles of every
+ *     (sequence, K/V head), in the order sequence, K/V head, tile, are cut
+ *     into W equal shares, one per wave, W = min(2048, B * Hkv *
+ *     ceil(Ncap / 64)) rounded up to a multiple of 4: every wave streams the
+ *     same number of tiles whatever the mix of lengths (the lengths are read
+ *     on the device); a share that spans several sequences or heads makes one
+ *     range per piece.
+ *   split > 0 (or B > 512): fixed ranges of `split` keys per wave (a multiple
+ *     of 64; for split = 0 the library's choice, attn_fp8_decode_split).
  * Sizes: (Hq / Hkv) * Sq <= 32 (so Sq <= scale_block), Ncap * D < 2^30,
- * B * Hkv <= 65535, ceil(Ncap / (4 * split')) <= 65535.  seqlens: device int32 [B] with Sq <= L_b <= Ncap; other
- * values give unspecified rows of that sequence (L_b is clamped to
- * [0, Ncap], so every access stays in bounds).
+ * B * Hkv <= 65535; fixed ranges: ceil(Ncap / (4 * split')) <= 65535.
+ * seqlens: device int32 [B] with Sq <= L_b <= Ncap; other values give
+ * unspecified rows of that sequence (L_b is clamped to [0, Ncap], so every
+ * access stays in bounds).
  */
 
-/* Keys per range used for `split` (0 = the library's choice: the largest
- * power of two in [64, 1024] that still gives 1024 workgroups of four
- * ranges over Ncap). */
+/* Keys per range of the fixed-range schedule for `split`, or 0 when the
+ * balanced shares are used (split = 0 and B <= 512).  For split = 0 and
+ * B > 512: the largest power of two in [64, 1024] that still gives 1024
+ * workgroups of four ranges over Ncap. */
 int attn_fp8_decode_split(int B, int Hkv, int Ncap, int split);
 
 /* Bytes of device workspace attn_fp8_decode needs (the per-range partials):
- * 4 * B * Hkv * ceil(Ncap / (4 * split')) * (Hq / Hkv) * Sq * (D + 2),
+ * balanced shares: 4 * (W + B * Hkv) * (Hq / Hkv) * Sq * (D + 2), W as above;
+ * fixed ranges: 4 * B * Hkv * ceil(Ncap / (4 * split')) * (Hq / Hkv) * Sq * (D + 2),
  * split' = attn_fp8_decode_split(B, Hkv, Ncap, split); 0 for invalid sizes. */
 size_t attn_fp8_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Ncap, int D, int split);
 
 /* attn_fp8_decode -- FP8 attention of Sq new queries per sequence against an
- * FP8 K/V cache.  Two launches on `stream`: the split kernel (one workgroup
- * per 4 ranges of one (sequence, K/V head); grid (B * Hkv, ranges / 4)) and
- * the merge.
+ * FP8 K/V cache.  Two launches on `stream`: the range kernel (balanced
+ * shares: W / 4 workgroups of four independent waves; fixed ranges: one
+ * workgroup per 4 ranges of one (sequence, K/V head), grid (B * Hkv,
+ * ranges / 4)) and the merge.
  *   workspace : device memory, 16-byte aligned, caller-owned, at least
  *               attn_fp8_decode_workspace_bytes(...) bytes; calls sharing a
  *               workspace must not overlap.
@@ -328,7 +341,7 @@ const char* attn_fp8_last_error(void);
 /* ABI version of this header (incremented on incompatible changes). */
 int attn_fp8_abi_version(void);
 
-#define ATTN_FP8_ABI_VERSION 4
+#define ATTN_FP8_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

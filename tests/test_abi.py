@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert fa.abi_version() == 4
+    assert fa.abi_version() == 5
     m = re.search(r"#define ATTN_FP8_ABI_VERSION (\d+)", open(HEADER).read())
     assert int(m.group(1)) == fa.abi_version()
 
@@ -248,18 +248,27 @@ def test_attn_fp8_decode_rejects(lib, kw, frag):
 
 
 def test_decode_split_and_workspace_size(lib):
-    # explicit splits pass through; the choice is a power of two in [64, 1024]
+    # explicit splits pass through (fixed ranges)
     assert fa.attn_fp8_decode_split(2, 2, 4096, 192) == 192
-    for B, Hkv, N in ((1, 1, 100), (2, 8, 4096), (16, 8, 32768), (64, 8, 131072), (1, 1, 1 << 20)):
+    # split 0 up to 512 sequences: the balanced shares (no fixed range)
+    for B, Hkv, N in ((1, 1, 100), (2, 8, 4096), (16, 8, 32768), (512, 1, 64)):
+        assert fa.attn_fp8_decode_split(B, Hkv, N) == 0
+    # split 0 above 512 sequences: fixed ranges, a power of two in [64, 1024]
+    for B, Hkv, N in ((513, 1, 100), (600, 8, 4096), (1024, 8, 32768), (4096, 1, 1 << 16)):
         s = fa.attn_fp8_decode_split(B, Hkv, N)
         assert s in (64, 128, 256, 512, 1024)
         nsplit = -(-N // (4 * s))
         assert B * Hkv * nsplit >= 1024 or s == 64
         assert s == 1024 or B * Hkv * -(-N // (8 * s)) < 1024          # the largest such power of two
-    assert fa.attn_fp8_decode_split(16, 8, 32768) == 1024
-    # partials: (D + 2) floats per (batch, K/V head, split, query row)
-    s = fa.attn_fp8_decode_split(2, 2, 4096)
-    assert fa.attn_fp8_decode_workspace_bytes(2, 8, 2, 1, 4096, 128) == 4 * 2 * 2 * -(-4096 // (4 * s)) * 4 * 130
+    # partials, (D + 2) floats per query row: balanced shares, one per wave and
+    # one per (sequence, K/V head); W = min(2048, tiles of a full cache), a multiple of 4
+    for B, Hq, Hkv, Sq, N, D in ((2, 8, 2, 1, 4096, 128), (16, 32, 8, 1, 32768, 128), (1, 1, 1, 1, 64, 64),
+                                 (3, 6, 3, 2, 200, 64)):
+        W = min(2048, B * Hkv * -(-N // 64))
+        W = -(-W // 4) * 4
+        assert fa.attn_fp8_decode_workspace_bytes(B, Hq, Hkv, Sq, N, D) == 4 * (W + B * Hkv) * (Hq // Hkv) * Sq * (D + 2)
+    # fixed ranges: per (batch, K/V head, range of four waves)
+    assert fa.attn_fp8_decode_workspace_bytes(2, 8, 2, 1, 4096, 128, 256) == 4 * 2 * 2 * -(-4096 // 1024) * 4 * 130
     assert fa.attn_fp8_decode_workspace_bytes(2, 8, 3, 1, 4096, 128) == 0
 
 

@@ -32,15 +32,33 @@ CASES = [
     (1, 8, 8, 1, 5000, 128, 128, True, True, [4097], 256, "iid"),
     (2, 16, 2, 4, 3000, 64, 128, True, True, [2999, 64], 0, "outlier"),
     (1, 1, 1, 1, 64, 128, 64, True, False, [1], 64, "iid"),
+    (1, 1, 1, 1, 64, 128, 64, True, False, [1], 0, "iid"),
+    # balanced shares (split 0): many short sequences, shares that cross
+    # (sequence, K/V head) segments, more than 64 sequences (several per lane
+    # of the length scan), more waves than tiles, lengths at Sq and at Ncap
+    (64, 4, 2, 1, 4096, 128, 128, True, True, ("rand", 1, 640), 0, "iid"),
+    (200, 2, 2, 2, 2048, 64, 64, True, True, ("rand", 2, 641), 0, "outlier"),
+    (300, 2, 1, 1, 256, 128, 128, False, False, ("rand", 1, 642), 0, "iid"),
+    # above the balanced schedule's batch limit: fixed ranges
+    (520, 1, 1, 1, 128, 64, 64, True, True, ("rand", 1, 643), 0, "iid"),
 ]
-IDS = ["B{}Hq{}Hkv{}Sq{}N{}D{}sb{}had{}c{}".format(*(int(x) if isinstance(x, bool) else x for x in c[:9]))
-       for c in CASES]
+IDS = ["B{}Hq{}Hkv{}Sq{}N{}D{}sb{}had{}c{}s{}".format(*(int(x) if isinstance(x, bool) else x
+                                                        for x in c[:9] + (c[10],))) for c in CASES]
+
+
+def _seqlens(spec, B, Ncap):
+    if isinstance(spec, tuple):                   # ("rand", lowest length, seed), the ends included
+        _, lo, seed = spec
+        L = np.random.default_rng(seed).integers(lo, Ncap + 1, size=B)
+        L[0], L[-1] = lo, Ncap
+        return L.astype(np.int32)
+    return np.asarray(spec, dtype=np.int32)
 
 
 def _run(case, seed_off=0):
     B, Hq, Hkv, Sq, Ncap, D, sb, had, causal, seqlens, split, kind = case
     q, k, v = workloads.generate_decode(kind, B, Hq, Hkv, Sq, Ncap, D, 60 + Ncap + seed_off)
-    seqlens = np.asarray(seqlens, dtype=np.int32)
+    seqlens = _seqlens(seqlens, B, Ncap)
     print(f"\n[decode] {case[:9]} seqlens {seqlens.tolist()} split {split}", flush=True)
     # the cache: the sequences' K and V quantised as one call would (Q slot unused)
     _, k8, v8, _, kd, vd = fa.quantize_qkv_fp8(dev(k), dev(k), dev(v), scale_block=sb, hadamard=had, seed=0x5EED)
@@ -49,7 +67,9 @@ def _run(case, seed_off=0):
     o, lse = fa.attn_fp8_decode(q8, qd, k8, v8, kd, vd, dev(seqlens), scale_block=sb, hadamard=had,
                                 causal=causal, split=split)
     torch.cuda.synchronize()
-    used = fa.attn_fp8_decode_split(B, Hkv, Ncap, split)
+    # (the diagnostic split loop: the kernel's fixed ranges, or one range per
+    # sequence for the balanced shares)
+    used = fa.attn_fp8_decode_split(B, Hkv, Ncap, split) or -(-Ncap // 64) * 64
     ref_k = oq.quantize_qkv(k, k, v, sb, had, 0x5EED)
     ref_q = oq.quantize_qkv(q, q, q, sb, had, 0x5EED)
     for g, r, nm in ((k8, ref_k[1], "k8"), (v8, ref_k[2], "v8"), (q8, ref_q[0], "q8")):
