@@ -447,10 +447,12 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_decode_balanced_kernel(Decode
   }
 }
 
+// Partials the merge loads in one round trip.
+constexpr int kCombineBatch = 32;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
   constexpr int PER = D / 64;                        // channels per lane
-  constexpr int UNROLL = 8;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= p.B * p.Hkv * p.MQ) return;             // (no barrier in this kernel)
@@ -484,42 +486,43 @@ __global__ __launch_bounds__(256) void attn_fp8_decode_combine(DecodeParams p) {
     L = L < 0 ? 0 : (L > p.Ncap ? p.Ncap : L);
     nx = (L + kWaves * p.split - 1) / (kWaves * p.split);
   }
-  // the splits' maxima, one split per lane
+  // kCombineBatch partials at a time: every load of a batch (this lane's (m, l)
+  // for partial x0 + lane, and the O rows of all the batch's partials) goes
+  // out before any arithmetic needs one, so a batch costs one round trip;
+  // the batches merge with a running maximum.
   float M = -INFINITY;
-  for (int x = lane; x < nx; x += 64) M = fmaxf(M, p.part_m[(base + x) * p.MQ + r]);
-  M = wave_max(M);
   float lsum = 0.0f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
-  for (int x0 = 0; x0 < nx; x0 += 64) {
-    // weights of 64 splits, one per lane, then O rows with independent loads
-    const int xl = x0 + lane;
-    float w = 0.0f;
-    if (xl < nx) {
-      w = __builtin_amdgcn_exp2f(p.part_m[(base + xl) * p.MQ + r] - M);
-      lsum += w * p.part_l[(base + xl) * p.MQ + r];
+  for (int x0 = 0; x0 < nx; x0 += kCombineBatch) {
+    const int n = nx - x0 < kCombineBatch ? nx - x0 : kCombineBatch;
+    float mi = -INFINITY, li = 0.0f;
+    if (lane < n) {
+      mi = p.part_m[(base + x0 + lane) * p.MQ + r];
+      li = p.part_l[(base + x0 + lane) * p.MQ + r];
     }
-    const int n = nx - x0 < 64 ? nx - x0 : 64;
-    int j = 0;
-    for (; j + UNROLL <= n; j += UNROLL) {
-      float vals[UNROLL][PER];
+    float vals[kCombineBatch][PER];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const size_t x = base + x0 + (u < n ? u : n - 1);      // (past the batch: a repeat, weight 0)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) vals[u][e] = p.part_o[((base + x0 + j + u) * p.MQ + r) * D + lane + 64 * e];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += wu * vals[u][e];
-      }
+      for (int e = 0; e < PER; ++e) vals[u][e] = p.part_o[(x * p.MQ + r) * D + lane + 64 * e];
     }
-    for (; j < n; ++j) {
-      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+    const float Mn = fmaxf(M, wave_max(mi));
+    const float f = __builtin_amdgcn_exp2f(M - Mn);          // 0 on the first batch
+    lsum *= f;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += wu * p.part_o[((base + x0 + j) * p.MQ + r) * D + lane + 64 * e];
+    for (int e = 0; e < PER; ++e) acc[e] *= f;
+    const float w = lane < n ? __builtin_amdgcn_exp2f(mi - Mn) : 0.0f;
+    lsum += w * li;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += wu * vals[u][e];
     }
+    M = Mn;
   }
   // row sum over the lanes
 #pragma unroll
