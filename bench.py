@@ -258,6 +258,25 @@ def main():
 
     fl_ms = median_ms(attn_fl, n_opt)
 
+    # ---- option: power-of-two scales per (scale block x 32 channels), the
+    # scaled MFMA's own granularity
+    mx32_out = (torch.empty_like(q8), torch.empty_like(k8), torch.empty_like(v8),
+                torch.empty((B, H, nb, D // 32), dtype=torch.float32, device=dev),
+                torch.empty((B, H, nb, D // 32), dtype=torch.float32, device=dev),
+                torch.empty((B, H, nb, D // 32), dtype=torch.float32, device=dev))
+    o_m32 = torch.empty_like(o)
+    l_m32 = torch.empty_like(lse)
+
+    def quant_mx32():
+        fa.quantize_qkv_fp8(q, k, v, scale_block=sb, hadamard=w.hadamard, seed=w.sign_seed, out=mx32_out, mx32=True)
+
+    def attn_mx32():
+        fa.attn_fp8_fwd(*mx32_out, scale_block=sb, hadamard=w.hadamard, causal=w.causal, out=(o_m32, l_m32),
+                        mx32=True)
+
+    quant_mx32()
+    m32_ms = median_ms(attn_mx32, n_opt)
+
     # ---- BF16 twin (inputs cast outside the timed region).  Timed after every
     # FP8 leg of this workload: at its MFMA load the chip lowers its clock, and
     # launches that follow soon after would inherit the lower clock.
@@ -274,6 +293,8 @@ def main():
     quant_mx()
     attn_mx()
     attn_fl()
+    quant_mx32()
+    attn_mx32()
     torch.cuda.synchronize()
 
     attn_tflops = flops / (attn_avg * 1e-3) / 1e12
@@ -311,6 +332,10 @@ def main():
                                   "frac_fp8_peak": round(flops / (fl_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
                                   "note": "attention alone, both options: power-of-two block scales and "
                                           "Schraudolph's exponential"},
+        "mx32_scales": {"tflops": round(flops / (m32_ms * 1e-3) / 1e12, 2), "ms": round(m32_ms, 4),
+                        "frac_fp8_peak": round(flops / (m32_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                        "note": "attention alone, power-of-two scales per (scale block x 32 channels) on the "
+                                "scaled FP8 MFMA"},
         "bf16_twin": {"tflops": round(flops / (bf16_ms * 1e-3) / 1e12, 2), "ms": round(bf16_ms, 4),
                       "frac_bf16_peak": round(flops / (bf16_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -333,7 +358,7 @@ def main():
         result["configs"], samples = configs_leg(args, fa, workloads, torch, dev, stream, w, (q, k, v), q_np, k_np,
                                                  v_np)
     if not args.no_cpu:
-        result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch, o_mx, o_fl))
+        result.update(cpu_leg(w, q_np, k_np, v_np, o, ob, o_sch, o_mx, o_fl, o_m32))
         if samples:
             config_accuracy(result["configs"], samples)
     print(json.dumps(result))
@@ -603,7 +628,7 @@ def hipcc_version():
         return None
 
 
-def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu, ofl_gpu):
+def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu, ofl_gpu, om32_gpu):
     """Oracle leg: time the FP64 reference on a bounded sample of the workload on
     the host cores and use the same reference rows for the accuracy report."""
     import numpy as np
@@ -646,7 +671,7 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu, ofl_gpu):
     else:
         pairs = len(rows) * w.N
     cpu_flops = 4 * w.D * pairs * len(heads)
-    e8, e16, es, emx, efl, ref_all = [], [], [], [], [], []
+    e8, e16, es, emx, efl, em32, ref_all = [], [], [], [], [], [], []
     for (b, h), (orf, _) in zip(heads, refs):
         g8 = o_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
         g16 = ob_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
@@ -658,10 +683,13 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu, ofl_gpu):
         gf = ofl_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
         efl.append((gf - orf[0, 0]).ravel())
         emx.append((gm - orf[0, 0]).ravel())
+        g32 = om32_gpu[b, h][rows].float().cpu().numpy().astype(np.float64)
+        em32.append((g32 - orf[0, 0]).ravel())
         ref_all.append(orf[0, 0].ravel())
     e8, e16, es, ra = np.concatenate(e8), np.concatenate(e16), np.concatenate(es), np.concatenate(ref_all)
     emx = np.concatenate(emx)
     efl = np.concatenate(efl)
+    em32 = np.concatenate(em32)
     rmse8 = float(np.sqrt(np.mean(e8 ** 2)))
     rmse16 = float(np.sqrt(np.mean(e16 ** 2)))
     rmses = float(np.sqrt(np.mean(es ** 2)))
@@ -675,6 +703,7 @@ def cpu_leg(w, q_np, k_np, v_np, o_gpu, ob_gpu, osch_gpu, omx_gpu, ofl_gpu):
                      "fp8_mx_rmse": float(np.sqrt(np.mean(emx ** 2))), "fp8_mx_cosine": cos(emx),
                      "fp8_mx_schraudolph_rmse": float(np.sqrt(np.mean(efl ** 2))),
                      "fp8_mx_schraudolph_cosine": cos(efl),
+                     "fp8_mx32_rmse": float(np.sqrt(np.mean(em32 ** 2))), "fp8_mx32_cosine": cos(em32),
                      "bound_ratio": 2.0, "rms_o": float(np.sqrt(np.mean(ra ** 2)))},
         "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": used,
                          "kind": "oracle", "cores_available": cores, "single_thread": single,

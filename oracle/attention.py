@@ -101,11 +101,11 @@ def emulated_fp8_attention(q8, k8, v8, q_descale, k_descale, v_descale,
 # descales), never from a kernel's blocking:
 #   * P is rounded to e4m3 before its product with V (reading C12; the pages
 #     do not model it).  A probability P in e4m3 moves by at most 2^-4 P
-#     (normal range) or min(P, 2^-10) (subnormal range), in units where the
-#     row's largest P is at least 1 (P carries no V factor: V's power-of-two
-#     scale is applied to V).  So |dO_id| <= sum_j [2^-4 w_ij
-#     + min(w_ij, 2^-10 / l_i)] |v_jd|, l_i the row sum against the row
-#     maximum (l_i >= 1).
+#     (normal range, P >= 2^-6) or min(P, 2^-10) (subnormal range), in units
+#     where the row's largest P is at least 1 (P carries no V factor: V's
+#     power-of-two scale is applied to V).  So |dO_id| <= sum_j b_ij |v_jd|
+#     with b_ij = 2^-4 w_ij where w_ij l_i >= 2^-6, else min(w_ij, 2^-10 / l_i),
+#     l_i the row sum against the row maximum (l_i >= 1).
 #   * The matrix cores sum the e4m3 products with the truncation of
 #     ``mfma_fp8``: each score moves by at most delta_ij (natural units);
 #     a row whose scores all move by at most D_i has its log-sum-exp moved by
@@ -216,22 +216,21 @@ def e1_rows_with_bars(q8r, dq, k8, dk, v8, dv, q_pos, causal, scale, exp2, accum
         acc_bar = np.zeros_like(o)
         grow = np.ones(len(m))
         lse_acc = np.zeros(len(m))
-    # P below e4m3's normal range: its rounding error is at most the smaller
-    # of P itself and half the smallest subnormal (P = w l, l >= 1)
-    cap = 2.0 ** -10 / l
+    # P's rounding per key, in weight units (P = w l in units where the row
+    # maximum is 1, l >= 1): at most 2^-4 P where P is in e4m3's normal range
+    # (P >= 2^-6), else at most the smaller of P itself and half the
+    # smallest subnormal 2^-10.  A key normal in these units is normal in any
+    # larger ones, and below 2^-6 the smaller of the two covers either range.
+    pw = w * l[:, None]
+    b = np.where(pw >= 2.0 ** -6, 2.0 ** -4 * w, np.minimum(w, 2.0 ** -10 / l[:, None]))
     absvv = np.abs(vv)
-    sub = np.empty_like(o)
-    sub2 = np.empty_like(o)
-    for i in range(o.shape[0]):
-        t = np.minimum(w[i], cap[i])[:, None] * absvv
-        sub[i] = t.sum(axis=0)
-        sub2[i] = (t * t).sum(axis=0)
-    var = (2.0 ** -8 / 3.0) * ((w * w) @ (vv * vv)) + sub2 / 3.0
+    pround = b @ absvv
+    var = ((b * b) @ (vv * vv)) / 3.0
     lse_bar = lse_acc.copy()
     if exp2 == "exact":
-        pbar = 2.0 ** -4 * wabs + sub
+        pbar = pround
     elif exp2 == "schraudolph":
-        pbar = ETA * wdev + (2.0 ** -4 * wabs + sub) * (1.0 + ETA)
+        pbar = ETA * wdev + pround * (1.0 + ETA)
         dev2 = np.empty_like(o)
         for i in range(o.shape[0]):
             dev2[i] = (w[i] * w[i]) @ (vv - o[i]) ** 2
@@ -372,6 +371,10 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     Schraudolph's bit-level approximation (``fastexp.schraudolph_exp2``) of
     t - m, as the kernel's option does: P = e4m3(S(t - m)) and l sums
     S(t - m).  The rescale 2^(m_old - m_new) stays exact.
+
+    Descales [..., nblk, D / g] (one per block and g channels, the 32-channel
+    MX form) scale each channel of Q and K before the dot product and each
+    channel of V in the product with P.
     """
     if exp2 not in ("exact", "schraudolph"):
         raise ValueError("exp2 must be 'exact' or 'schraudolph'")
@@ -390,17 +393,28 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
     nkb = -(-n // block_c)
     o_all = np.empty(lead + (len(row_idx), d))
     lse_all = np.empty(lead + (len(row_idx),))
+    grouped = kd.ndim == len(lead) + 2
     for idx in np.ndindex(*lead):
         qh, kh, vh = q[idx][row_idx], k[idx], v[idx]
         qdr = qd[idx][row_idx // scale_block]
+        if grouped:
+            g = d // kd.shape[-1]
+            qh = qh * np.repeat(qdr, g, axis=1)
+            qdr = np.ones(len(row_idx))
         m = np.full(len(row_idx), -np.inf)
         l = np.zeros(len(row_idx))
         acc = np.zeros((len(row_idx), d))
         for j in range(nkb):
             k0, k1 = j * block_c, min(n, (j + 1) * block_c)
             sb = k0 // scale_block
-            s = qh @ kh[k0:k1].T
-            t = s * (qdr * kd[idx][sb] * score_scale)[:, None]
+            if grouped:
+                s = qh @ (kh[k0:k1] * np.repeat(kd[idx][sb], g)[None, :]).T
+                t = s * (qdr * score_scale)[:, None]
+                vs = vh[k0:k1] * np.repeat(vd[idx][sb], g)[None, :]
+            else:
+                s = qh @ kh[k0:k1].T
+                t = s * (qdr * kd[idx][sb] * score_scale)[:, None]
+                vs = vh[k0:k1] * vd[idx][sb]
             if causal:
                 t = np.where(np.arange(k0, k1)[None, :] <= row_idx[:, None], t, -np.inf)
             tmax = t.max(axis=1)
@@ -414,7 +428,7 @@ def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, sc
             pu[~ok] = 0.0
             pq = e4m3.decode(e4m3.encode(pu)) if quantize_p else pu
             l = alpha * l + pu.sum(axis=1)
-            acc = alpha[:, None] * acc + pq @ (vh[k0:k1] * vd[idx][sb])
+            acc = alpha[:, None] * acc + pq @ vs
         o_all[idx] = acc / l[:, None]
         lse_all[idx] = math.log(2.0) * (m + np.log2(l))
     if bf16_output:
