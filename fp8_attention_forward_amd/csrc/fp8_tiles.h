@@ -14,10 +14,13 @@ namespace attnfp8 {
 constexpr float kTau = 8.8f;
 // When the reference moves it is set kLift below the tile maximum (log2
 // units, a whole number): the key that moved it gets P = 2^kLift, which e4m3
-// holds exactly, and the small probabilities sit 2^kLift higher, away from
-// e4m3's subnormal range.  The headroom kTau - kLift decides how closely the
-// reference follows the running maximum.
-constexpr float kLift = 4.0f;
+// holds exactly (a fractional lift would round the largest P of the row),
+// and the small probabilities sit 2^kLift higher, away from e4m3's subnormal
+// range.  The headroom kTau - kLift decides how closely the reference follows
+// the running maximum: a larger lift moves it more often (each move costs the
+// tile maximum, an O rescale and P formed again).  2 gave the smallest
+// P-rounding error on outlier inputs, with half the moves of 4.
+constexpr float kLift = 2.0f;
 
 // Exponentials of the probabilities P.
 //   kExpExact: v_exp_f32 of the scaled score (one FMA + one transcendental).

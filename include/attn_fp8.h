@@ -128,9 +128,10 @@ int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v,
  *                       O = softmax(Q K^T / sqrt(D)) V of the dequantised inputs.
  *   lse           out : float32 [B][H][N], natural log of sum_j exp(q_i.k_j / sqrt(D)).
  * Arithmetic: e4m3 x e4m3 products with FP32 accumulation, FP32 statistics,
- * P re-quantised to e4m3 on chip (P = 2^(t - m) <= 256 against a per-row
- * reference m, which moves only when a key block would exceed 256, and then
- * to 2^4 below that block's maximum).
+ * P re-quantised to e4m3 on chip (P = 2^(t - m) <= 2^8.8 ~ 445.7, inside
+ * e4m3's range, against a per-row reference m in log2 units, which moves
+ * only when a key block would exceed that, and then to 2 below that block's
+ * maximum: the key that moved it gets P = 4).
  */
 int attn_fp8_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  const float* q_descale, const float* k_descale, const float* v_descale,

@@ -340,7 +340,7 @@ def brute_force_attention(q, k, v, causal, scale):
 
 def emulated_fp8_attention_tiled(q8, k8, v8, q_descale, k_descale, v_descale, scale_block, hadamard,
                                  causal, rows=None, tau=8.8, quantize_p=True, bf16_output=True, block_c=64,
-                                 exp2="exact", lift=4.0):
+                                 exp2="exact", lift=2.0):
     """E2 (a diagnostic, not the contract): the running-softmax loop over key
     blocks with P re-quantised to e4m3, in the FP8 kernel's blocking.
 

@@ -39,7 +39,7 @@ TILE = 64
 
 
 def emulated_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_block, hadamard, causal,
-                        split, tau=8.8, quantize_p=True, bf16_output=True, lift=4.0):
+                        split, tau=8.8, quantize_p=True, bf16_output=True, lift=2.0):
     """Decode of [B][Hq][Sq][D] query codes against the FP8 cache, in the
     kernel's key ranges (a diagnostic; the contract is E1,
     ``emulated_fp8_decode_bars``).  Returns (O [B][Hq][Sq][D], LSE [B][Hq][Sq])
