@@ -18,8 +18,9 @@ constexpr float kTau = 8.8f;
 // and the small probabilities sit 2^kLift higher, away from e4m3's subnormal
 // range.  The headroom kTau - kLift decides how closely the reference follows
 // the running maximum: a larger lift moves it more often (each move costs the
-// tile maximum, an O rescale and P formed again).  2 gave the smallest
-// P-rounding error on outlier inputs, with half the moves of 4.
+// tile maximum, an O rescale and P formed again) and rounds small P less
+// coarsely.  2 moves it on 4% of the steps of outlier inputs against 10% for
+// a lift of 4, for a P-rounding error 13% larger.
 constexpr float kLift = 2.0f;
 
 // Exponentials of the probabilities P.
