@@ -2,7 +2,8 @@
 
 Each case draws its shape and options from a fixed seed: sequence lengths
 (ragged against the 64-key and 128-query tiles), head dimension, scale block,
-rotation, causal mask, the MX and Schraudolph options, document lengths
+rotation, causal mask, the MX options (block and 32-channel scales) and
+Schraudolph's exponential, document lengths
 (packed path) and cache lengths, grouping and new-token counts (decode).
 The bars are those of the fixed-shape tests: quantiser bit-exact, O / LSE
 against E1 (the exact attention of the quantised inputs) within RMSE 2e-3 and
@@ -34,17 +35,25 @@ def _draw(seed):
                      exp2="schraudolph" if rng.random() < 0.3 else "exact")
 
 
-@pytest.mark.parametrize("seed", range(12))
+def _mx32(seed):
+    # (drawn from a stream of its own, so the other draws of a seed stay as they were)
+    return bool(np.random.default_rng(seed + 7919).random() < 0.3)
+
+
+@pytest.mark.parametrize("seed", range(16))
 def test_dense_sweep(seed):
     rng, c = _draw(1000 + seed)
     B, H, N = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 900))
-    print(f"\n[dense sweep {seed}] B{B} H{H} N{N} {c}", flush=True)
+    m32 = _mx32(seed)
+    if m32:
+        c["mx"] = False
+    print(f"\n[dense sweep {seed}] B{B} H{H} N{N} {c} mx32={m32}", flush=True)
     q, k, v = workloads.generate("outlier", B, H, N, c["D"], 5000 + seed)
-    qq = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=c["sb"], hadamard=c["had"], mx=c["mx"])
+    qq = fa.quantize_qkv_fp8(dev(q), dev(k), dev(v), scale_block=c["sb"], hadamard=c["had"], mx=c["mx"], mx32=m32)
     o, lse = fa.attn_fp8_fwd(*qq, scale_block=c["sb"], hadamard=c["had"], causal=c["causal"], exp2=c["exp2"],
-                             mx=c["mx"])
+                             mx=c["mx"], mx32=m32)
     torch.cuda.synchronize()
-    ref = oq.quantize_qkv(q, k, v, c["sb"], c["had"], 0x5EED, pow2=c["mx"])
+    ref = oq.quantize_qkv(q, k, v, c["sb"], c["had"], 0x5EED, pow2=c["mx"] or m32, group=32 if m32 else None)
     for g, r in zip(qq, ref):
         g = host(g)
         assert np.array_equal(g if r.dtype == np.uint8 else g.view(np.uint32),
