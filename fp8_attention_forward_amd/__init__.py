@@ -344,8 +344,9 @@ def attn_fp8_decode(q8, q_descale, k8, v8, k_descale, v_descale, seqlens, scale_
     """Decode: q8 [B, Hq, Sq, D] uint8 with q_descale [B, Hq] or [B, Hq, 1]; cache k8, v8 [B, Hkv, Ncap, D]
     with descales [B, Hkv, ceil(Ncap / scale_block)]; seqlens int32 [B] (device).
 
-    Returns (o [B, Hq, Sq, D] bfloat16, lse [B, Hq, Sq] float32).  split: keys per range (0 = library's
-    choice); workspace: optional uint8 device tensor (allocated here if None).
+    Returns (o [B, Hq, Sq, D] bfloat16, lse [B, Hq, Sq] float32).  split: 0 = the library's choice (balanced
+    per-wave shares of the batch's key tiles up to 512 sequences, fixed ranges above), > 0 = fixed ranges of
+    that many keys per wave; workspace: optional uint8 device tensor (allocated here if None).
     """
     lib = load_library()
     B, Hq, Sq, D = _shape4(q8, "q8")
