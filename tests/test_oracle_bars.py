@@ -20,6 +20,9 @@ against computations that do not share their arithmetic:
     accumulation model gives (``mfma_fp8.scores``) lies within ``acc_bar`` of
     E1, on unrotated channel outliers, where the truncation is largest; and a
     crafted row where it moves O measurably stays inside too.
+(d) The decode step's and the packed documents' forms of the bars hold their
+    own kernel-shaped loops (key ranges merged by log-sum-exp; documents as
+    sequences of their own).
 """
 
 import math
@@ -153,3 +156,45 @@ def test_accumulation_bar_is_zero_free_only_where_products_are_cut():
     assert np.all(mfma_fp8.scores(q8[0, 0], k8[0, 0]) == e4m3.decode(q8[0, 0]) @ e4m3.decode(k8[0, 0]).T)
     rel = bars["acc_bar"] / np.maximum(np.abs(bars["o"]), 1e-30)
     assert float(np.median(rel)) < 1e-4
+
+
+@pytest.mark.parametrize("split", [64, 192, 4096])
+def test_decode_split_loop_lies_within_the_decode_bars(split):
+    # the decode step's bars (E1 of every (sequence, query head), no split)
+    # hold the kernel-shaped loop on key ranges merged by log-sum-exp
+    from oracle import decode as od
+    rng = np.random.default_rng(split)
+    B, Hq, Hkv, Sq, Ncap, D, sb = 2, 4, 2, 3, 700, 128, 64
+    q = rng.standard_normal((B, Hq, Sq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, Ncap, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, Ncap, D)).astype(np.float32)
+    m = rng.random(v.shape) < 0.01
+    v[m] = (10.0 * rng.standard_normal(int(m.sum()))).astype(np.float32)
+    seqlens = np.array([700, 301], np.int32)
+    _, k8, v8, _, kd, vd = oq.quantize_qkv(k, k, v, sb, True, 5)
+    q8, _, _, qd, _, _ = oq.quantize_qkv(q, q, q, sb, True, 5)
+    bars = od.emulated_fp8_decode_bars(q8, qd, k8, v8, kd, vd, seqlens, sb, True, True)
+    o2, l2 = od.emulated_fp8_decode(q8, qd, k8, v8, kd, vd, seqlens, sb, True, True, split, bf16_output=False)
+    err = np.abs(o2 - bars["o"])
+    assert np.all(err <= bars["pbar"] + 1e-12 * (1.0 + np.abs(bars["o"])))
+    assert np.all(np.abs(l2 - bars["lse"]) <= bars["lse_bar"] + 1e-9 * (1.0 + np.abs(bars["lse"])))
+    assert float(np.max(err / bars["pbar"])) > 0.05
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_documents_loop_lies_within_the_packed_bars(causal):
+    # per document, the kernel-shaped loop against the per-document E1 bars
+    from oracle import varlen as ov
+    rng = np.random.default_rng(int(causal))
+    H, D, sb = 2, 64, 64
+    lens = [0, 1, 130, 64, 257]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    q, k, v = (rng.standard_normal((H, T, D)).astype(np.float32) for _ in range(3))
+    qq = ov.quantize_qkv_varlen(q, k, v, cu, sb, True, 9)
+    bars = ov.emulated_fp8_attention_varlen_bars(*qq, cu, sb, True, causal)
+    o2, l2 = ov.emulated_fp8_attention_varlen(*qq, cu, sb, True, causal, bf16_output=False)
+    err = np.abs(o2 - bars["o"])
+    assert np.all(err <= bars["pbar"] + 1e-12 * (1.0 + np.abs(bars["o"])))
+    assert np.all(np.abs(l2 - bars["lse"]) <= bars["lse_bar"] + 1e-9 * (1.0 + np.abs(bars["lse"])))
+    assert float(np.max(err / bars["pbar"])) > 0.05
