@@ -107,8 +107,8 @@ int quantize_qkv_fp8(const float* q, const float* k, const float* v,
 #define ATTN_FP8_MX32 8u
 
 /* quantize_qkv_fp8_opts -- quantize_qkv_fp8 with option flags (quantize_qkv_fp8
- * is this call with flags = 0).  flags: ATTN_FP8_MX, ATTN_FP8_MX32 or 0; any
- * other bit -> ATTN_EINVAL. */
+ * is this call with flags = 0).  flags: ATTN_FP8_MX, ATTN_FP8_MX32 or 0
+ * (with both set, ATTN_FP8_MX32 applies); any other bit -> ATTN_EINVAL. */
 int quantize_qkv_fp8_opts(const float* q, const float* k, const float* v,
                           int B, int H, int N, int D, int scale_block, int hadamard, uint64_t seed,
                           unsigned flags, uint8_t* q8, uint8_t* k8, uint8_t* v8,

@@ -126,6 +126,22 @@ def test_quantize_opts_flags(lib):
     assert int(m.group(1)) == fa.ATTN_FP8_MX
 
 
+def test_mx32_flag_is_known_to_the_dense_calls_only(lib):
+    assert fa.ATTN_FP8_MX32 == int(re.search(r"#define ATTN_FP8_MX32 (\d+)u", open(HEADER).read()).group(1))
+    a = [P, P, P, 1, 1, 64, 128, 128, 1, 1]
+    # dense: a known flag, so validation goes on to the pointers
+    assert lib.quantize_qkv_fp8_opts(*a, fa.ATTN_FP8_MX32, P, P, NUL, P, P, P, None) == fa.ATTN_EINVAL
+    assert "v8 is NULL" in fa.last_error()
+    args = [P, P, P, P, P, P, 1, 1, 64, 128, 128, 1, 0]
+    assert lib.attn_fp8_fwd_opts(*args, fa.ATTN_FP8_MX32, NUL, P, None) == fa.ATTN_EINVAL
+    assert "o_bf16 is NULL" in fa.last_error()
+    # packed documents: not an option there
+    cu = P
+    assert lib.quantize_qkv_fp8_varlen(P, P, P, cu, 1, 1, 128, 128, 128, 1, 1, fa.ATTN_FP8_MX32,
+                                       P, P, P, P, P, P, None) == fa.ATTN_EINVAL
+    assert "unknown flags" in fa.last_error()
+
+
 def test_rejects_heads_too_long_for_32_bit_offsets(lib):
     assert _a(lib, N=1 << 23, D=128) == fa.ATTN_EINVAL
     assert "N * D" in fa.last_error()
