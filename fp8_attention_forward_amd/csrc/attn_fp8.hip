@@ -115,6 +115,7 @@ struct Fp8State {
   float m_ref;     // reference max (log2 units)
   float l_acc;     // this lane's half of the row sum
   v8i pop;         // P^T of the last tile in e4m3 (B operand of the P V product)
+  int move_run;    // (wave-uniform) consecutive tiles that moved the reference
 };
 
 // The rows of one attention sequence as the loop sees them.
@@ -211,6 +212,10 @@ __device__ __forceinline__ bool move_reference(const STile<D>& s, Fp8State<D>& s
   return true;
 }
 
+// Tiles in a row that moved the reference after which the next tile's
+// maximum is taken before its exponentials
+constexpr int kMaxFirstRun = 2;
+
 // Largest P (<= 2^kTau) the reference allows without moving, less a margin
 // for the rounding of the exponent argument (|m| < 2^14).
 constexpr float kMoveBound = 445.7218f * (1.0f - 1.0f / 64.0f);
@@ -231,19 +236,34 @@ constexpr float kMoveBound = 445.7218f * (1.0f - 1.0f / 64.0f);
 // the reference has settled; always on the first tile, whose reference is
 // -1e30 and whose P overflow to +inf).  When the reference does move, P_t is
 // formed again, and each P is then at most 2^kLift.  The decisions are those of taking
-// the maximum of every tile.  Schraudolph's exponential cannot be formed
-// first: past 2^128 its bits run into the sign field instead of saturating,
-// so there the maximum is taken before the exponentials, on every tile.
+// the maximum of every tile.  Moves come in runs on some inputs (scores that
+// keep growing along the keys): after two steps in a row that moved, the
+// wave takes the maximum first and forms P once, which makes the same
+// decisions (a move needs a P above 2^tau, and such a P trips the test) at
+// the cost of one maximum when the run has ended.  Schraudolph's exponential cannot be
+// formed first: past 2^128 its bits run into the sign field instead of
+// saturating, so there the maximum is taken before the exponentials, on
+// every tile.
 template <int D, int EXPM>
 __device__ __forceinline__ void fp8_phaseA(const STile<D>& s, Fp8State<D>& st, float c) {
   float alpha = 1.0f;
   float rs, q4;
   if constexpr (EXPM == kExpExact) {
-    rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
-    // (written so that a NaN also counts)
-    if (__builtin_amdgcn_ballot_w64(!(q4 <= kMoveBound))) {
-      if (move_reference<D>(s, st, c, alpha)) rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
+    bool take_max = st.move_run >= kMaxFirstRun;
+    bool have_p = false;
+    if (!take_max) {
+      rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
+      have_p = true;
+      // (written so that a NaN also counts)
+      take_max = __builtin_amdgcn_ballot_w64(!(q4 <= kMoveBound)) != 0;
     }
+    bool moved = false;
+    if (take_max) {
+      moved = move_reference<D>(s, st, c, alpha);
+      if (moved) have_p = false;
+    }
+    st.move_run = moved ? st.move_run + 1 : 0;
+    if (!have_p) rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
   } else {
     move_reference<D>(s, st, c, alpha);
     rs = p_tile<D, EXPM>(s, st.pop, c, -st.m_ref, &q4);
@@ -383,6 +403,7 @@ __device__ __forceinline__ void attn_fp8_seq(const Fp8SeqView& seq, int qt) {
   st.m_ref = -1e30f;
   st.l_acc = 0.0f;
   st.pop = (v8i){};
+  st.move_run = kMaxFirstRun;      // (the first tile always moves the reference)
 
   // per-tile score scale
   auto c_of = [&](int t) { return MX ? c_q : c_q * kd[(t < n_kt ? t : n_kt - 1) / TPB]; };
