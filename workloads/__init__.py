@@ -86,6 +86,15 @@ def generate(kind, B, H, N, D, seed):
             ch = rng.choice(D, size=4, replace=False)
             for t in (q, k):
                 t[:, h, :, ch] = np.float32(30.0) * t[:, h, :, ch] + np.float32(5.0)
+    elif kind == "ramp":
+        # Q and K share one unit direction u per head; K's component along u
+        # grows by 0.25 per token, so every query's scores rise along the keys
+        # (by about 16 log2 units per 64-key tile at D = 128 with Q's 10 u):
+        # the running maximum climbs on every key tile
+        u = rng.standard_normal(size=(B, H, 1, D)).astype(np.float32)
+        u /= np.linalg.norm(u, axis=-1, keepdims=True).astype(np.float32)
+        q += np.float32(10.0) * u
+        k += (np.float32(0.25) * np.arange(N, dtype=np.float32))[None, None, :, None] * u
     elif kind != "iid":
         raise ValueError(f"unknown workload kind {kind!r}")
     return q, k, v
